@@ -1,0 +1,157 @@
+"""Pins for the oracle's router and permutation: brute force on every token,
+closed forms, library softmax and invariants (no GPU)."""
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+
+
+def _brute_topk(lrow, k):
+    """Rank of e = number of experts with a larger logit, or an equal logit and a lower index."""
+    l = np.where(lrow == 0, 0.0, lrow.astype(np.float64))
+    E = l.size
+    rank = np.array([np.sum((l > l[e]) | ((l == l[e]) & (np.arange(E) < e))) for e in range(E)])
+    out = np.full(k, -1)
+    for e in range(E):
+        if rank[e] < k:
+            out[rank[e]] = e
+    return out
+
+
+def _adversarial_logits(E, rng):
+    rows = [
+        np.zeros(E, np.float32),                                           # all equal
+        np.full(E, -3.25, np.float32),
+        np.where(np.arange(E) % 2 == 0, 0.0, -0.0).astype(np.float32),    # +0 / -0 mix
+        np.repeat(rng.standard_normal(E // 4 + 1), 4)[:E].astype(np.float32),  # ties in groups of 4
+        np.concatenate([np.full(3, 5.0), np.full(E - 3, 1.0)]).astype(np.float32),  # ties across boundary
+        rng.permutation(np.arange(E, dtype=np.float32)),
+        np.round(rng.standard_normal(E) * 2).astype(np.float32),           # many integer ties
+    ]
+    r = rng.standard_normal(E).astype(np.float32)
+    r[E - 1] = r.max() + 1                                                # max at the last index
+    r[E - 2] = r[E - 1]                                                   # duplicated maximum
+    rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("E,K", [(16, 4), (256, 8), (7, 7), (256, 1), (64, 8)])
+def test_route_ids_match_brute_force(E, K):
+    rng = np.random.default_rng(E * 100 + K)
+    L = np.concatenate([(rng.standard_normal((40, E)) * 1.4).astype(np.float32),
+                        _adversarial_logits(E, rng)])
+    ids, _ = oracle.route(L, K)
+    for t in range(L.shape[0]):
+        np.testing.assert_array_equal(ids[t], _brute_topk(L[t], K), err_msg=f"row {t}")
+
+
+def test_route_all_equal_gives_first_k():
+    ids, w = oracle.route(np.zeros((3, 256), np.float32), 8)
+    np.testing.assert_array_equal(ids, np.tile(np.arange(8), (3, 1)))
+    np.testing.assert_array_equal(w, np.float32(1 / 8))
+
+
+def test_route_k1_weight_is_one():
+    rng = np.random.default_rng(0)
+    _, w = oracle.route(rng.standard_normal((50, 256)).astype(np.float32), 1)
+    np.testing.assert_array_equal(w, np.float32(1.0))
+
+
+def test_route_k_equals_e_is_softmax():
+    rng = np.random.default_rng(1)
+    L = (rng.standard_normal((30, 16)) * 2).astype(np.float32)
+    ids, w = oracle.route(L, 16)
+    ref = scipy.special.softmax(L.astype(np.float64), axis=1)
+    got = np.zeros_like(ref)
+    np.put_along_axis(got, ids.astype(np.int64), w.astype(np.float64), axis=1)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-7)
+
+
+def test_route_weights_closed_form_and_sum():
+    rng = np.random.default_rng(2)
+    L = (rng.standard_normal((200, 256)) * 1.43).astype(np.float32)
+    ids, w = oracle.route(L, 8)
+    l = np.take_along_axis(L.astype(np.float64), ids.astype(np.int64), 1)
+    ref = np.exp(l - l[:, :1]) / np.exp(l - l[:, :1]).sum(1, keepdims=True)
+    np.testing.assert_allclose(w, ref, rtol=0, atol=1e-7)
+    np.testing.assert_allclose(w.astype(np.float64).sum(1), 1.0, atol=1e-6)
+    assert np.all(np.diff(w, axis=1) <= 0)  # slots ordered by rank
+
+
+def test_route_weights_ignore_unselected_logits():
+    rng = np.random.default_rng(4)
+    L = (rng.standard_normal((100, 256)) * 1.43).astype(np.float32)
+    ids, w = oracle.route(L, 8)
+    L2 = L.copy()
+    kth = np.take_along_axis(L, ids[:, 7:8].astype(np.int64), 1)
+    mask = np.ones_like(L, bool)
+    np.put_along_axis(mask, ids.astype(np.int64), False, 1)
+    L2[mask] = (kth - 5.0 - rng.random(L.shape).astype(np.float32))[mask]  # push the rest further down
+    ids2, w2 = oracle.route(L2, 8)
+    np.testing.assert_array_equal(ids, ids2)
+    np.testing.assert_allclose(w, w2, rtol=0, atol=1e-7)
+
+
+# --- permutation -------------------------------------------------------------------------
+
+def _check_permutation(ids, e0, e_loc):
+    T, K = ids.shape
+    off, rt, rs, tr = oracle.permute(ids, e0, e_loc)
+    local = (ids >= e0) & (ids < e0 + e_loc)
+    M = int(local.sum())
+    assert off[0] == 0 and off[-1] == M and np.all(np.diff(off) >= 0)
+    assert rt.size == M and rs.size == M
+    for el in range(e_loc):  # each expert's block: its pairs in ascending token order
+        r0, r1 = off[el], off[el + 1]
+        tt, kk = np.nonzero(ids == e0 + el)
+        np.testing.assert_array_equal(rt[r0:r1], tt)
+        np.testing.assert_array_equal(rs[r0:r1], kk)
+    for t in range(T):
+        for k in range(K):
+            if local[t, k]:
+                r = tr[t, k]
+                assert rt[r] == t and rs[r] == k
+            else:
+                assert tr[t, k] == -1
+    # permute then unpermute is the identity on token-row payloads
+    payload = np.arange(T * 3).reshape(T, 3)
+    rows = payload[rt]
+    back = np.full((T, K, 3), -1)
+    back[local] = rows[tr[local]]
+    np.testing.assert_array_equal(back[local], np.broadcast_to(payload[:, None, :], (T, K, 3))[local])
+    return off, rt, rs, tr
+
+
+def test_permute_invariants_random():
+    rng = np.random.default_rng(6)
+    L = rng.standard_normal((300, 64)).astype(np.float32)
+    ids, _ = oracle.route(L, 8)
+    _check_permutation(ids, 0, 64)
+    _check_permutation(ids, 16, 8)  # a local window, pairs elsewhere are dropped
+
+
+def test_permute_all_tokens_one_expert():
+    T, K = 50, 4
+    ids = np.tile(np.array([3, 0, 1, 2]), (T, 1)).astype(np.int32)
+    off, rt, rs, tr = _check_permutation(ids, 0, 8)
+    np.testing.assert_array_equal(off, [0, 50, 100, 150, 200, 200, 200, 200, 200])
+    np.testing.assert_array_equal(rt[150:200], np.arange(T))
+    np.testing.assert_array_equal(rs[150:200], 0)
+
+
+def test_permute_identity_special_case():
+    """K=1 and e = t mod E: rows are token t at row (t mod E) * (T/E) + t // E."""
+    T, E = 64, 16
+    ids = (np.arange(T) % E).reshape(T, 1).astype(np.int32)
+    off, rt, rs, tr = _check_permutation(ids, 0, E)
+    np.testing.assert_array_equal(off, np.arange(E + 1) * (T // E))
+    t = np.arange(T)
+    np.testing.assert_array_equal(tr[:, 0], (t % E) * (T // E) + t // E)
+
+
+def test_permute_no_local_pairs():
+    ids = np.full((10, 2), 40, np.int32)
+    ids[:, 1] = 41
+    off, rt, rs, tr = _check_permutation(ids, 0, 32)
+    assert off[-1] == 0 and np.all(tr == -1)
