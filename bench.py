@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""MoE-layer throughput of libdmoe on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
+
+A step is one dmoe_forward over one batch of synthetic input: router logits
+(or given logits) -> route -> permute -> [quantise x] -> gate/up + SwiGLU ->
+[quantise h] -> down -> shared expert -> combine. Inputs and weights are
+resident in HBM before the timed region. The default workload is the BF16
+decode layer at full dots3-note shape (T=64 tokens, hidden 5120, 256 routed +
+1 shared experts, top-8, expert FFN 1536). Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s / FP8 TFLOP/s vs peak, 1 MI355X"
+PEAK_HBM_GBPS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def build_layer(cfg, dev):
+    import synth
+    from fp8_expert_ffn_amd import MoELayer
+    layer = MoELayer(cfg.H, cfg.F, cfg.F_s, cfg.E, cfg.E_loc, cfg.e0, cfg.K, cfg.dtype, dev)
+    bf16 = cfg.dtype == "bf16"
+    for which in ("gate", "up", "down"):
+        synth.fill_expert_weights(cfg, which, cfg.experts, lambda i, a, w=which: layer.set_weight(w, i, a), bf16)
+        if cfg.F_s:
+            draw = synth.expert_weight_bf16 if bf16 else synth.expert_weight_f32
+            layer.set_weight(which, -1, draw(cfg, which, synth.SHARED))
+    return layer
+
+
+def accounting(cfg, offsets: np.ndarray, logits_computed: bool) -> dict:
+    """Algorithmic FLOPs and bytes of the layer and of its gate/up launch, on the real routing."""
+    es = 1 if cfg.dtype == "fp8" else 2
+    counts = np.diff(offsets)
+    M = int(offsets[-1])
+    touched = int((counts > 0).sum())
+    H, F, Fs, T, Ts, E = cfg.H, cfg.F, cfg.F_s, cfg.T, cfg.T_s, cfg.E
+    nb = lambda n: -(-n // 128)  # noqa: E731
+    sc = 4 if cfg.dtype == "fp8" else 0  # FP8 block scales (FP32 per 128x128 block)
+    w_gu = 2 * (F * H * es + nb(F) * nb(H) * sc)          # one expert's gate + up
+    w_d = H * F * es + nb(H) * nb(F) * sc
+    ws_gu = 2 * (Fs * H * es + nb(Fs) * nb(H) * sc) if Fs and Ts else 0
+    ws_d = (H * Fs * es + nb(H) * nb(Fs) * sc) if Fs and Ts else 0
+    flops = 2.0 * M * 3 * H * F + (2.0 * Ts * 3 * H * Fs if Fs else 0.0)
+    if logits_computed:
+        flops += 2.0 * T * H * E
+    bytes_ = touched * (w_gu + w_d) + ws_gu + ws_d + T * H * 2 + T * H * 2  # weights + x read + y written
+    bytes_ += E * H * 4 if logits_computed else T * E * 4                  # router weight or given logits
+    gu_flops = 2.0 * M * 2 * H * F
+    gu_bytes = touched * w_gu + T * H * es + M * F * 2                     # weights + A rows once + h written
+    return dict(M=M, touched=touched, flops=flops, bytes=bytes_, gu_flops=gu_flops, gu_bytes=gu_bytes)
+
+
+def cpu_baseline(cfg, x_bits, wr, given, seconds: float) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload's tokens."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    get = (lambda w, e: synth.expert_weight_f32(cfg, w, e)) if cfg.dtype == "fp8" else \
+        (lambda w, e: synth.expert_weight_bf16(cfg, w, e))
+    rng = np.random.default_rng(7)
+    done, n, t0 = 0, 2, time.perf_counter()
+    while True:
+        tok = np.sort(rng.choice(cfg.T, size=min(n, cfg.T), replace=False))
+        oracle.moe_forward(cfg, x_bits, get, w_r=wr, logits=given, tokens=tok)
+        done += tok.size
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= cfg.T:
+            break
+        n = min(cfg.T, max(1, int(tok.size * max(1.0, (seconds - el) / max(el, 1e-3)) * 0.5)))
+    return {"value": done / el, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"{done} tokens of the {cfg.name} workload (random token subsets, each token's full "
+                      f"layer output incl. per-expert weight preparation), {el:.1f}s on "
+                      f"{platform.processor() or platform.machine()}; BLAS threads {blas}, elementwise NumPy "
+                      f"single-threaded"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=1, help="workload index (0 tiny, 1 decode, 2 prefill, "
+                                                                "3 EP share, 4 non-divisible)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the multi-GPU exchange "
+              f"is not part of this library)", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import fp8_expert_ffn_amd as dm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = synth.config(args.workload)
+    t0 = time.time()
+    layer = build_layer(cfg, dev)
+    x_bits = synth.x_bf16(cfg)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    if cfg.logits == "router":
+        wr, given = synth.router_weight(cfg), None
+        kw = dict(w_router=torch.from_numpy(wr).to(dev))
+    else:
+        wr, given = None, synth.given_logits(cfg)
+        kw = dict(logits=torch.from_numpy(given).to(dev))
+    torch.cuda.synchronize()
+    log(f"[bench] {cfg.name}: weights and inputs resident after {time.time() - t0:.1f}s")
+
+    d, p, ws, out = layer.make_call(x, cfg.T_s, **kw)
+    stream = torch.cuda.current_stream()
+    nstage = dm.DMOE_STAGES + 1
+    for _ in range(args.warmup):
+        dm.dmoe_forward(d, p, ws)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nstage)] for _ in range(args.steps)]
+    for row in ev:
+        for e in row:
+            e.record(stream)  # creates the underlying HIP events
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        dm.dmoe_forward_timed(d, p, ws, ev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    h1 = time.perf_counter()
+    ms_step = start.elapsed_time(end) / args.steps
+    stage_ms = {name: float(np.mean([ev[i][s].elapsed_time(ev[i][s + 1]) for i in range(args.steps)]))
+                for s, name in enumerate(dm.STAGE_NAMES)}
+    log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (host {1e3 * (h1 - h0) / args.steps:.4f} ms/step)")
+    log("[bench] stages (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
+
+    offsets = layer.ws_view(d, ws, "offsets").cpu().numpy()
+    acc = accounting(cfg, offsets, cfg.logits == "router")
+    sec = ms_step / 1e3
+    gu_sec = stage_ms["gateup"] / 1e3
+    gu_time_hbm = acc["gu_bytes"] / (PEAK_HBM_GBPS * 1e9)
+    gu_time_mfma = acc["gu_flops"] / (PEAK_TFLOPS[cfg.dtype] * 1e12)
+    if gu_time_hbm >= gu_time_mfma:
+        achieved = acc["gu_bytes"] / gu_sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None}
+    else:
+        achieved = acc["gu_flops"] / gu_sec / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_TFLOPS[cfg.dtype], 4), "traffic": None}
+    roof["kernel"] = f"gemm_tile_kernel<{cfg.dtype}, gate/up> (routed experts)"
+    roof["alg_bytes_per_launch"] = acc["gu_bytes"]
+    roof["alg_flops_per_launch"] = acc["gu_flops"]
+    roof["avg_launch_ms"] = round(stage_ms["gateup"], 5)
+
+    result = {
+        "metric": METRIC,
+        "value": round(cfg.T / sec, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "F": cfg.F, "F_s": cfg.F_s, "E": cfg.E,
+                   "E_loc": cfg.E_loc, "e0": cfg.e0, "K": cfg.K, "T_s": cfg.T_s, "logits": cfg.logits,
+                   "M": acc["M"], "touched_experts": acc["touched"], "parallelism": "single GPU"},
+        "layer": {"alg_bytes": acc["bytes"], "alg_flops": acc["flops"],
+                  "GBps": round(acc["bytes"] / sec / 1e9, 1),
+                  "TFLOPs": round(acc["flops"] / sec / 1e12, 2),
+                  "frac_hbm": round(acc["bytes"] / sec / 1e9 / PEAK_HBM_GBPS, 4),
+                  "frac_mfma": round(acc["flops"] / sec / 1e12 / PEAK_TFLOPS[cfg.dtype], 4)},
+        "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, x_bits, wr, given, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,74 @@
+"""Build libdmoe.so in-tree with hipcc for gfx950.
+
+    python -m fp8_expert_ffn_amd.build [-v]
+
+Every HIP source under csrc/ is compiled to an object with -fPIC and linked
+into fp8_expert_ffn_amd/libdmoe.so. Packed FP32 instructions are disabled for
+all device code (target feature -packed-fp32-ops).
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+LIB = os.path.join(HERE, "libdmoe.so")
+OBJDIR = os.path.join(HERE, "_build")
+ARCH = os.environ.get("DMOE_OFFLOAD_ARCH", "gfx950")
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
+    "-I", INCLUDE,
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC)")
+
+
+def sources() -> list[str]:
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def _run(cmd: list[str], verbose: bool) -> None:
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = (r.stdout + r.stderr).strip()
+    # hipcc's host pass does not know the packed-fp32 feature; that note is harmless
+    lines = [l for l in out.splitlines() if "packed-fp32-ops" not in l or "error" in l.lower()]
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n" + "\n".join(lines))
+    if verbose and lines:
+        print("\n".join(lines), flush=True)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source and link libdmoe.so; returns the library path."""
+    cc = hipcc()
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1, 8))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = [ex.submit(_run, [cc, *HIPCC_FLAGS, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
+        for f in futs:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,69 @@
+// Internal launchers between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <algorithm>
+#include <stdint.h>
+
+#include "../../include/dmoe.h"
+#include "dmoe_device.h"
+
+namespace dmoe {
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+inline int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }
+
+// route.hip
+hipError_t launch_router_logits(const uint16_t* x, int64_t ldx, const float* w_r, int T, int H, int E,
+                                float* logits, hipStream_t stream);
+hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w, hipStream_t stream);
+
+// permute.hip
+constexpr int kPermutePairs = 512;  // (token, slot) pairs per permutation block
+size_t permute_ws_bytes(int T, int K, int E_loc);
+hipError_t launch_permute(const int32_t* ids, int T, int K, int e0, int E_loc, int32_t* offsets,
+                          int32_t* row_token, int32_t* row_slot, int32_t* token_row, void* ws,
+                          hipStream_t stream);
+
+// quant.hip
+hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                            float* scales, int64_t lds, hipStream_t stream);
+hipError_t launch_quant_weight_blocks(const float* w, int rows, int cols, int64_t ldw, uint8_t* q, int64_t ldq,
+                                      float* scales, hipStream_t stream);
+
+// gemm.hip
+struct GemmArgs {
+  int dtype;              // DMOE_BF16 / DMOE_FP8_E4M3
+  const void* a;          // activations (BF16 or E4M3 codes)
+  int64_t lda;            // elements
+  const float* a_scales;  // FP8: per row and 128-column slice
+  int64_t ldas;
+  const int32_t* row_token;  // gather map for the A rows (NULL: identity)
+  const int32_t* offsets;    // [E_loc + 1]
+  int E_loc;
+  int max_rows;
+  const void* w0;  // gate (gate/up) or down weights
+  const void* w1;  // up (gate/up only)
+  int64_t ldw;     // elements
+  const float* ws0;
+  const float* ws1;
+  int K;           // reduction length (valid): H for gate/up, F for down
+  int N;           // valid output columns: F for gate/up, H for down
+  uint16_t* out;   // BF16 [rows, ldo]
+  int64_t ldo;
+  void* ws;               // tile schedule (gemm_ws_bytes)
+  bool scheduled = false; // true: ws already holds the schedule for these offsets and max_rows
+};
+size_t gemm_ws_bytes(int max_rows, int E_loc);
+hipError_t launch_schedule(const int32_t* offsets, int E_loc, int max_rows, void* ws, hipStream_t stream);
+hipError_t launch_gemm_gateup(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_fill_offsets(int32_t* offsets, int rows, hipStream_t stream);
+
+// combine.hip
+hipError_t launch_combine(const uint16_t* o, int64_t ldo, const int32_t* token_row, const float* w,
+                          const uint16_t* s, int64_t lds, int T_s, int T, int K, int H, uint16_t* y, int64_t ldy,
+                          hipStream_t stream);
+
+}  // namespace dmoe

@@ -1,0 +1,113 @@
+// Fine-grained FP8 quantisation: dynamic 1x128 activation slices and 128x128
+// weight blocks, E4M3 codes with one FP32 scale each (Transformers PR #47844,
+// implementation list: dynamic activations, E4M3 weights, 128 x 128 weight
+// block size; validation list and the authors' reply: partial blocks when a
+// dimension is not a multiple of 128).
+//
+// Rule for a slice or block: s = f32(amax / 448) with a correctly rounded
+// FP32 division; code = E4M3 round-to-nearest-even of f32(v / s), saturated at
+// +-448, sign bit kept; s == 0 gives all-zero codes. Partial slices and
+// blocks take the amax over their valid elements only.
+#include "dmoe_internal.h"
+
+namespace dmoe {
+
+__device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, b); }
+
+// 16 lanes per 128-column slice, 8 BF16 values (16 bytes) per lane; 16 slices
+// per 256-thread workgroup.
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int rows, int cols,
+                                                        int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                                                        float* __restrict__ scales, int64_t lds) {
+  const int nsl = (cols + 127) >> 7;
+  const int64_t slice = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (slice >= (int64_t)rows * nsl) return;  // whole 16-lane groups leave together
+  const int sub = threadIdx.x & 15;
+  const int64_t r = slice / nsl;
+  const int j = (int)(slice - r * nsl);
+  const int c0 = j * 128 + sub * 8;
+  const bool valid = c0 < cols;  // cols % 8 == 0: a chunk is wholly valid or wholly padding
+  float v[8];
+  if (valid) {
+    const i32x4 raw = *reinterpret_cast<const i32x4*>(x + r * ldx + c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32((uint32_t)raw[i] & 0xffffu);
+      v[2 * i + 1] = bf16_to_f32((uint32_t)raw[i] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = wave_max_width(amax, 16);
+  const float s = div_rn(amax, 448.f);
+  uint32_t lo = 0, hi = 0;
+  if (s != 0.f && valid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(div_rn(v[i], s)) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(div_rn(v[4 + i], s)) << (8 * i);
+  }
+  *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(lo, hi);
+  if (sub == 0) scales[r * lds + j] = s;
+}
+
+hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                            float* scales, int64_t lds, hipStream_t stream) {
+  const int64_t slices = (int64_t)rows * ((cols + 127) / 128);
+  if (slices == 0) return hipSuccess;
+  quant_act_kernel<<<(unsigned)ceil_div(slices, 16), 256, 0, stream>>>(x, rows, cols, ldx, q, ldq, scales, lds);
+  return hipGetLastError();
+}
+
+// One workgroup per 128x128 block (weight preparation, not on the timed path).
+__global__ __launch_bounds__(256) void quant_weight_blocks_kernel(const float* __restrict__ w, int rows, int cols,
+                                                                  int64_t ldw, uint8_t* __restrict__ q,
+                                                                  int64_t ldq, float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int br = blockIdx.y, bc = blockIdx.x;
+  const int r0 = br * 128, c0 = bc * 128;
+  // each thread: 4 consecutive columns of 16 rows
+  const int cc = (threadIdx.x & 31) * 4;
+  const int rr = threadIdx.x >> 5;  // 0..7
+  float amax = 0.f;
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + rr + 8 * i;
+    const int c = c0 + cc;
+    if (r < rows && c < cols) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(w + (int64_t)r * ldw + c);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fabsf(v[k]));  // cols % 4 == 0
+    }
+  }
+  amax = wave_max_width(amax, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = div_rn(amax, 448.f);
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + rr + 8 * i;
+    const int c = c0 + cc;
+    uint32_t word = 0;
+    if (r < rows && c < cols && s != 0.f) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(w + (int64_t)r * ldw + c);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) word |= e4m3_encode(div_rn(v[k], s)) << (8 * k);
+    }
+    *reinterpret_cast<uint32_t*>(q + (int64_t)r * ldq + c) = word;
+  }
+  if (threadIdx.x == 0) scales[(int64_t)br * gridDim.x + bc] = s;
+}
+
+hipError_t launch_quant_weight_blocks(const float* w, int rows, int cols, int64_t ldw, uint8_t* q, int64_t ldq,
+                                      float* scales, hipStream_t stream) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(cols, 128), (unsigned)ceil_div(rows, 128));
+  quant_weight_blocks_kernel<<<grid, 256, 0, stream>>>(w, rows, cols, ldw, q, ldq, scales);
+  return hipGetLastError();
+}
+
+}  // namespace dmoe

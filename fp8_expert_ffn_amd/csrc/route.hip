@@ -1,0 +1,217 @@
+// Router: FP32 logits on matrix cores, then top-K selection and renormalised
+// softmax weights, one wavefront per token.
+//
+// FP32 routing: Transformers PR #47844, implementation list. Top-K with
+// renormalised weights: Transformers docs "Dots3Note", Dots3NoteTextConfig
+// (num_experts_per_tok, norm_topk_prob, routed_scaling_factor, n_group,
+// topk_group); the softmax scoring is the reading of the docs' "post-softmax"
+// router_logits entry.
+#include "dmoe_internal.h"
+
+namespace dmoe {
+
+// ---------------------------------------------------------------------------
+// Router logits L = f32(x) . W_r^T.
+//
+// x is BF16 (8 significant bits). Each FP32 router weight is split exactly as
+// w = hi + mid + lo with three BF16 values (truncation: hi keeps the top 8
+// significand bits, mid the next 8, lo the last 8), so every product x*part is
+// exact in FP32 and the three BF16 MFMAs sum exactly the products of the FP32
+// definition, with FP32 accumulation.
+//
+// Wave tile: (16*TT tokens) x (16*EE experts); the 4 waves of a workgroup split
+// H into quarters and their partial tiles are added in wave order through LDS
+// (fixed order: deterministic).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void split3_bf16(const float (&w)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t b = __float_as_uint(w[i]);
+    const float h = __uint_as_float(b & 0xffff0000u);
+    const float r1 = w[i] - h;  // exact
+    const float m = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+    const float r2 = r1 - m;  // exact, fits in 8 significant bits
+    hi[i] = __builtin_bit_cast(__bf16, (uint16_t)(b >> 16));
+    mid[i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(m) >> 16));
+    lo[i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(r2) >> 16));
+  }
+}
+
+template <int TT, int EE>
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                            const float* __restrict__ w_r, int T, int H, int E,
+                                                            float* __restrict__ logits) {
+  __shared__ f32x4 red[3][TT * EE][kWave];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 16 * TT;
+  const int e0 = blockIdx.y * 16 * EE;
+  const int r16 = lane & 15;
+  const int kg = (lane >> 4) * 8;
+  const int kq = H / 4;
+  const int kbeg = wave * kq;
+
+  const uint16_t* xrow[TT];
+  bool xok[TT];
+#pragma unroll
+  for (int i = 0; i < TT; ++i) {
+    const int t = t0 + 16 * i + r16;
+    xok[i] = t < T;
+    xrow[i] = x + (int64_t)(xok[i] ? t : 0) * ldx + kg;
+  }
+  const float* wrow[EE];
+  bool wok[EE];
+#pragma unroll
+  for (int j = 0; j < EE; ++j) {
+    const int e = e0 + 16 * j + r16;
+    wok[j] = e < E;
+    wrow[j] = w_r + (int64_t)(wok[j] ? e : 0) * H + kg;
+  }
+
+  f32x4 acc[TT][EE];
+#pragma unroll
+  for (int i = 0; i < TT; ++i)
+#pragma unroll
+    for (int j = 0; j < EE; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k = kbeg; k < kbeg + kq; k += 32) {
+    bf16x8 a[TT];
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+      i32x4 v = xok[i] ? *reinterpret_cast<const i32x4*>(xrow[i] + k) : i32x4{0, 0, 0, 0};
+      a[i] = __builtin_bit_cast(bf16x8, v);
+    }
+#pragma unroll
+    for (int j = 0; j < EE; ++j) {
+      float wv[8];
+      if (wok[j]) {
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wrow[j] + k);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wrow[j] + k + 4);
+        wv[0] = w0[0]; wv[1] = w0[1]; wv[2] = w0[2]; wv[3] = w0[3];
+        wv[4] = w1[0]; wv[5] = w1[1]; wv[6] = w1[2]; wv[7] = w1[3];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) wv[q] = 0.f;
+      }
+      bf16x8 hi, mid, lo;
+      split3_bf16(wv, hi, mid, lo);
+#pragma unroll
+      for (int i = 0; i < TT; ++i) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], hi, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], mid, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], lo, acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < TT; ++i)
+#pragma unroll
+      for (int j = 0; j < EE; ++j) red[wave - 1][i * EE + j][lane] = acc[i][j];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int i = 0; i < TT; ++i) {
+#pragma unroll
+    for (int j = 0; j < EE; ++j) {
+      f32x4 s = acc[i][j];
+      s += red[0][i * EE + j][lane];
+      s += red[1][i * EE + j][lane];
+      s += red[2][i * EE + j][lane];
+      const int e = e0 + 16 * j + r16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 16 * i + (lane >> 4) * 4 + r;
+        if (t < T && e < E) logits[(int64_t)t * E + e] = s[r];
+      }
+    }
+  }
+}
+
+hipError_t launch_router_logits(const uint16_t* x, int64_t ldx, const float* w_r, int T, int H, int E,
+                                float* logits, hipStream_t stream) {
+  if (T <= 256) {
+    dim3 grid((T + 15) / 16, (E + 15) / 16);
+    router_logits_kernel<1, 1><<<grid, 256, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
+  } else {
+    dim3 grid((T + 63) / 64, (E + 63) / 64);
+    router_logits_kernel<4, 4><<<grid, 256, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Top-K selection: one wavefront per token; lane l holds experts l, l+64, ...
+// Each logit becomes a 64-bit key (order-preserving image of the FP32 value
+// in the high word, ~expert in the low word), so the maximum key is the
+// largest value with the lowest index among equals. K rounds of a wave-wide
+// maximum pick the slots in rank order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t route_key(float v, uint32_t e) {
+  if (v == 0.f) v = 0.f;  // -0.0 -> +0.0
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)~e;
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  const uint32_t b = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
+  return __uint_as_float(b);
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int K,
+                                                    int32_t* __restrict__ ids, float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (int64_t)t * E;
+  uint64_t key[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? route_key(row[e], (uint32_t)e) : 0ull;  // 0 sorts below every finite key
+  }
+  uint64_t mine = 0;
+  for (int k = 0; k < K; ++k) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint64_t o = shfl_xor_u64(best, off);
+      best = o > best ? o : best;
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (key[i] == best) key[i] = 0ull;
+    if (lane == k) mine = best;
+  }
+  // Weights: exp(l_k - l_max) / sum over the selected set, in double, rounded once.
+  const float v = key_value(mine);
+  const float vmax = __shfl(v, 0);
+  double ex = lane < K ? exp((double)v - (double)vmax) : 0.0;
+  double sum = ex;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += shfl_xor_f64(sum, off);
+  if (lane < K) {
+    ids[(int64_t)t * K + lane] = (int32_t)(~(uint32_t)mine);
+    wts[(int64_t)t * K + lane] = (float)(ex / sum);
+  }
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w, hipStream_t stream) {
+  const dim3 grid((T + 3) / 4);
+  const int vpl = (E + 63) / 64;
+  if (vpl <= 1) route_kernel<1><<<grid, 256, 0, stream>>>(logits, T, E, K, ids, w);
+  else if (vpl <= 2) route_kernel<2><<<grid, 256, 0, stream>>>(logits, T, E, K, ids, w);
+  else if (vpl <= 4) route_kernel<4><<<grid, 256, 0, stream>>>(logits, T, E, K, ids, w);
+  else if (vpl <= 8) route_kernel<8><<<grid, 256, 0, stream>>>(logits, T, E, K, ids, w);
+  else route_kernel<16><<<grid, 256, 0, stream>>>(logits, T, E, K, ids, w);
+  return hipGetLastError();
+}
+
+}  // namespace dmoe

@@ -1,0 +1,279 @@
+/*
+ * libdmoe: the hot path of one dots3-note preview mixture-of-experts layer on
+ * an AMD Instinct MI355X (gfx950).
+ *
+ * The layer (model card "dots-studio/dots3-note-prev", Model Overview table;
+ * Transformers docs "Dots3Note", Dots3NoteTextConfig parameters): 256 routed
+ * experts plus 1 shared expert, top-8 token-choice routing with renormalised
+ * weights, hidden size 5120, per-expert SwiGLU FFN of width 1536, in BF16 or in
+ * fine-grained FP8 (E4M3 weights with one FP32 scale per 128x128 block and
+ * dynamically quantised 1x128 activations, including weight dimensions that
+ * are not multiples of 128: Transformers PR #47844, implementation and
+ * validation lists).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All data pointers are DEVICE pointers unless stated otherwise; the caller
+ *   owns every buffer (including workspaces). The library never allocates,
+ *   frees or synchronises; it enqueues kernels on `stream` and returns.
+ * - Matrices are row-major with an explicit pitch ("ld", in elements).
+ *   BF16 values are passed as their 16-bit patterns (uint16_t).
+ * - Arguments are validated on the host before anything is enqueued; an
+ *   invalid call returns a non-zero status, enqueues nothing and writes
+ *   nothing. dmoe_last_error() then describes the problem (per thread).
+ * - Launch failures are reported as DMOE_ERR_HIP. Faults inside kernels
+ *   surface at the caller's next synchronisation, as with any HIP call.
+ * - Device buffers must be 16-byte aligned and pitches multiples of 8
+ *   elements (16 for FP8 codes) unless stated otherwise.
+ * - Outputs must not alias inputs. Calls on different streams may run
+ *   concurrently when their buffers are disjoint. Results are bitwise
+ *   reproducible run to run.
+ * - No entry point reads device memory from the host, so every call can be
+ *   captured into a HIP graph. Grids are sized from host-known bounds and
+ *   kernels read the actual counts on the device.
+ *
+ * Weight layout (produced once, before timing, by the preparation calls)
+ * ------------------------------------------------------------------
+ * Expert e's gate and up weights are [F_pad, ldw] blocks at
+ * w + e * F_pad * ldw, F_pad = round_up(F, 128); down weights are [H, ldw]
+ * blocks at w + e * H * ldw with ldw >= round_up(F, 128). Rows F..F_pad-1 and
+ * columns past the valid width are zero (codes 0x00 or BF16 +0). FP8 block
+ * scales are dense [E_loc][ceil(rows/128)][ceil(cols/128)] FP32 arrays over the
+ * valid (unpadded) rows and columns. The hidden size H must be a multiple of
+ * 128 (5120 on the pages).
+ */
+#ifndef DMOE_H
+#define DMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipEvent_t* hipEvent_t;
+
+typedef int32_t dmoe_status;
+#define DMOE_OK 0
+#define DMOE_ERR_INVALID_ARG 1 /* bad size, null pointer, out-of-range index */
+#define DMOE_ERR_ALIGNMENT 2   /* pointer or pitch not aligned as required */
+#define DMOE_ERR_UNSUPPORTED 3 /* valid request this build does not implement */
+#define DMOE_ERR_WORKSPACE 4   /* workspace null or smaller than required */
+#define DMOE_ERR_HIP 5         /* a HIP launch or runtime call failed */
+
+#define DMOE_BF16 1
+#define DMOE_FP8_E4M3 2
+
+#define DMOE_ABI_VERSION 1
+
+/* Text of the last error on this thread ("" if none). Host pointer, valid
+ * until the next call on the same thread. */
+const char* dmoe_last_error(void);
+
+/* DMOE_ABI_VERSION of the built library. */
+int32_t dmoe_abi_version(void);
+
+/*
+ * Router logits, FP32: logits[t, e] = sum_h f32(x[t, h]) * w_r[e, h].
+ * Follows: Transformers docs "Dots3Note", router_logits output of shape
+ * (batch*seq, num_experts); FP32 routing (PR #47844, implementation list).
+ * x: [T, ldx] BF16; w_r: [E, H] FP32 dense; logits: [T, E] FP32 dense.
+ * The sum is accumulated in FP32 on matrix cores (each product exact); its
+ * order differs from a sequential sum, so results agree with an exact sum to
+ * FP32 accumulation error, not bit for bit.
+ * Requires 1 <= E <= 1024, H % 128 == 0, T >= 0 (T == 0 is a no-op).
+ */
+dmoe_status dmoe_router_logits(const uint16_t* x, int64_t ldx, const float* w_r, int32_t T, int32_t H,
+                               int32_t E, float* logits, hipStream_t stream);
+
+/*
+ * Top-K routing (Dots3NoteTextConfig: num_experts_per_tok, norm_topk_prob,
+ * routed_scaling_factor = 1, n_group = topk_group = 1).
+ * For each token: the K largest logits, equal values going to the lower expert
+ * index, -0.0 treated as +0.0; slot k holds the expert of rank k.
+ * topk_w[t, k] = exp(l_k - l_max) / sum_{j in top-K} exp(l_j - l_max), i.e. the
+ * softmax over all E experts renormalised over the selected K, rounded to FP32.
+ * logits: [T, E] FP32 (finite values; NaN behaviour is undefined);
+ * topk_ids: [T, K] int32; topk_w: [T, K] FP32.
+ * Requires 1 <= K <= E <= 1024, K <= 64.
+ */
+dmoe_status dmoe_route(const float* logits, int32_t T, int32_t E, int32_t K, int32_t* topk_ids, float* topk_w,
+                       hipStream_t stream);
+
+/*
+ * Expert-contiguous permutation of the (token, slot) pairs routed to this
+ * GPU's experts [e0, e0 + E_loc): a stable counting sort over the flat pair
+ * index t*K + k, so rows are ordered by (local expert, token).
+ * Outputs: offsets [E_loc + 1] (offsets[E_loc] = M, the number of local
+ * pairs); row_token [T*K] and row_slot [T*K] (entries [0, M) written);
+ * token_row [T*K] (row of pair (t, k), or -1 if its expert is not local).
+ * Expert ids outside [e0, e0 + E_loc) are simply not local.
+ * ws: device workspace of at least dmoe_permute_ws_bytes(T, K, E_loc) bytes.
+ */
+size_t dmoe_permute_ws_bytes(int32_t T, int32_t K, int32_t E_loc);
+dmoe_status dmoe_permute(const int32_t* topk_ids, int32_t T, int32_t K, int32_t e0, int32_t E_loc,
+                         int32_t* offsets, int32_t* row_token, int32_t* row_slot, int32_t* token_row, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Dynamic 1x128 activation quantisation to E4M3 (PR #47844: dynamic
+ * activations; partial blocks per its validation list).
+ * For row r and column slice j = [128j, min(128j + 128, cols)):
+ *   amax = max |x|, s = f32(amax / 448) (correctly rounded),
+ *   q = E4M3 round-to-nearest-even of f32(x / s), saturated to +-448,
+ *   sign bit of x / s kept; if s == 0 every code of the slice is 0x00.
+ * x: [rows, ldx] BF16; q: [rows, ldq] uint8 codes (columns [cols, round_up(cols,
+ * 128)) are written as 0x00 and must fit in ldq); scales: [rows, lds] FP32
+ * with ceil(cols/128) valid entries per row. Requires cols % 8 == 0.
+ */
+dmoe_status dmoe_quant_act(const uint16_t* x, int32_t rows, int32_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                           float* scales, int64_t lds, hipStream_t stream);
+
+/*
+ * Weight preparation (not part of the timed layer): 128x128 block quantisation
+ * of one FP32 weight matrix w [rows, ldw] to E4M3 codes, with the same
+ * amax/448 rule over each block's valid elements.
+ * q: [round_up(rows, 128), ldq] codes, ldq >= round_up(cols, 128); padding rows
+ * and columns are written as 0x00. scales: [ceil(rows/128), ceil(cols/128)]
+ * FP32 dense. Requires cols % 4 == 0, ldw % 4 == 0.
+ */
+dmoe_status dmoe_quant_weight_blocks(const float* w, int32_t rows, int32_t cols, int64_t ldw, uint8_t* q,
+                                     int64_t ldq, float* scales, hipStream_t stream);
+
+/*
+ * Grouped gate/up projection with fused SwiGLU over the permuted rows:
+ * for local expert e and row r in [offsets[e], offsets[e+1]):
+ *   a_r = a[row_token[r]] (or a[r] when row_token is NULL),
+ *   g = a_r . Wg_e^T, u = a_r . Wu_e^T, h[r, :] = bf16(silu(g) * u).
+ * BF16: a is [*, lda] BF16, weights BF16, FP32 accumulation.
+ * FP8: a is [*, lda] E4M3 codes with scales a_scales [*, ldas] (one per 128
+ * columns), weights E4M3 with block scales; each 128-wide K slice's code
+ * product is scaled by a_scale * w_scale and added in FP32.
+ * h: [max_rows, ldh] BF16, ldh >= round_up(F, 128); columns [F, round_up(F,
+ * 128)) are written as 0. Rows past offsets[E_loc] are not written.
+ * max_rows: host-side upper bound on offsets[E_loc] (T*K for routed rows),
+ * used only to size the grid. ws: at least dmoe_gemm_ws_bytes(max_rows, E_loc).
+ */
+size_t dmoe_gemm_ws_bytes(int32_t max_rows, int32_t E_loc);
+dmoe_status dmoe_grouped_gemm_gateup(int32_t dtype, const void* a, int64_t lda, const float* a_scales,
+                                     int64_t ldas, const int32_t* row_token, const int32_t* offsets,
+                                     int32_t E_loc, int32_t max_rows, const void* w_gate, const void* w_up,
+                                     int64_t ldw, const float* w_scales_gate, const float* w_scales_up, int32_t H,
+                                     int32_t F, uint16_t* h, int64_t ldh, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
+/*
+ * Grouped down projection: o[r, :] = bf16(h_r . Wd_e^T) for the rows of each
+ * local expert, with the same FP8 block-scale rule over K = F (the last K
+ * slice may be partial; padded columns of h and Wd are zero).
+ * h: [max_rows, ldh] BF16 or E4M3 codes (+ h_scales [max_rows, ldhs]);
+ * o: [max_rows, ldo] BF16.
+ */
+dmoe_status dmoe_grouped_gemm_down(int32_t dtype, const void* h, int64_t ldh, const float* h_scales, int64_t ldhs,
+                                   const int32_t* offsets, int32_t E_loc, int32_t max_rows, const void* w_down,
+                                   int64_t ldw, const float* w_scales_down, int32_t F, int32_t H, uint16_t* o,
+                                   int64_t ldo, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Shared expert (Dots3NoteTextConfig n_shared_experts = 1,
+ * shared_experts_intermediate_size): s_out[t] = bf16(down(q(bf16(silu(gate a_t)
+ * * up a_t)))) for tokens t in [0, T_s), i.e. the routed expert computation
+ * with one group of T_s rows and the identity row map. a/a_scales as in the
+ * gate/up call; weights in the single-expert layout above; s_out [T_s, lds_out].
+ * ws: at least dmoe_shared_expert_ws_bytes(dtype, T_s, H, F_s).
+ */
+size_t dmoe_shared_expert_ws_bytes(int32_t dtype, int32_t T_s, int32_t H, int32_t F_s);
+dmoe_status dmoe_shared_expert(int32_t dtype, const void* a, int64_t lda, const float* a_scales, int64_t ldas,
+                               int32_t T_s, const void* w_gate, const void* w_up, const void* w_down,
+                               int64_t ldw_gu, int64_t ldw_d, const float* w_scales_gate,
+                               const float* w_scales_up, const float* w_scales_down, int32_t H, int32_t F_s,
+                               uint16_t* s_out, int64_t lds_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Deterministic gather combine:
+ *   y[t] = bf16( sum_{k=0..K-1, token_row[t,k] >= 0} topk_w[t,k] * o[token_row[t,k]]
+ *                + (t < T_s ? s_out[t] : 0) ),
+ * accumulated in FP32 in slot order, no atomics. s_out may be NULL (T_s
+ * ignored). o: [*, ldo] BF16; y: [T, ldy] BF16.
+ */
+dmoe_status dmoe_combine(const uint16_t* o, int64_t ldo, const int32_t* token_row, const float* topk_w,
+                         const uint16_t* s_out, int64_t lds, int32_t T_s, int32_t T, int32_t K, int32_t H,
+                         uint16_t* y, int64_t ldy, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Whole layer: router logits (unless given) -> route -> permute -> [FP8:
+ * quantise x] -> gate/up + SwiGLU -> [FP8: quantise h] -> down -> shared
+ * expert -> combine. One stream, no host synchronisation.
+ * ------------------------------------------------------------------------- */
+typedef struct dmoe_layer_desc {
+  int32_t T;            /* tokens */
+  int32_t H;            /* hidden size, multiple of 128 */
+  int32_t F;            /* routed expert FFN width */
+  int32_t F_s;          /* shared expert FFN width (0: no shared expert) */
+  int32_t E;            /* routed experts in the model */
+  int32_t E_loc;        /* experts held here: [e0, e0 + E_loc) */
+  int32_t e0;
+  int32_t K;            /* experts per token */
+  int32_t T_s;          /* the shared expert runs on tokens [0, T_s) */
+  int32_t dtype;        /* DMOE_BF16 or DMOE_FP8_E4M3 */
+  int32_t logits_given; /* 1: ptrs.logits is an input; 0: computed from x and w_router */
+} dmoe_layer_desc;
+
+typedef struct dmoe_layer_ptrs {
+  const uint16_t* x; /* [T, ldx] BF16 */
+  int64_t ldx;
+  const float* w_router; /* [E, H] FP32 (when logits are computed) */
+  float* logits;         /* [T, E] FP32: output, or input when logits_given */
+  const void* w_gate;    /* routed experts, layout above */
+  const void* w_up;
+  const void* w_down;
+  int64_t ldw_gu, ldw_d;
+  const float* ws_gate; /* FP8 block scales (NULL for BF16) */
+  const float* ws_up;
+  const float* ws_down;
+  const void* sw_gate; /* shared expert, same layout with one expert */
+  const void* sw_up;
+  const void* sw_down;
+  int64_t ldsw_gu, ldsw_d;
+  const float* sws_gate;
+  const float* sws_up;
+  const float* sws_down;
+  int32_t* topk_ids; /* [T, K] output */
+  float* topk_w;     /* [T, K] output */
+  uint16_t* y;       /* [T, ldy] BF16 output */
+  int64_t ldy;
+} dmoe_layer_ptrs;
+
+size_t dmoe_forward_ws_bytes(const dmoe_layer_desc* desc);
+dmoe_status dmoe_forward(const dmoe_layer_desc* desc, const dmoe_layer_ptrs* ptrs, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/*
+ * dmoe_forward, recording caller-created events between its stages so a
+ * profiler or benchmark can time each stage on the stream it runs on.
+ * stage_events: host array of DMOE_STAGES + 1 hipEvent_t; event i is recorded
+ * before stage i and event DMOE_STAGES after the last one. Stages, in order:
+ * 0 router logits (empty when logits are given), 1 route, 2 permute and tile
+ * schedule, 3 quantise x (FP8), 4 gate/up + SwiGLU, 5 quantise h (FP8),
+ * 6 down, 7 shared expert, 8 combine. Recording events adds stream markers
+ * only; the results are identical to dmoe_forward.
+ */
+#define DMOE_STAGES 9
+dmoe_status dmoe_forward_timed(const dmoe_layer_desc* desc, const dmoe_layer_ptrs* ptrs, void* ws, size_t ws_bytes,
+                               hipStream_t stream, hipEvent_t* stage_events);
+
+/*
+ * Views into the forward workspace, for inspection after dmoe_forward (host
+ * byte offsets from ws; -1 if the buffer does not exist for this desc):
+ * 0 offsets, 1 row_token, 2 row_slot, 3 token_row, 4 x codes, 5 x scales,
+ * 6 h (BF16), 7 h codes, 8 h scales, 9 o, 10 shared output.
+ */
+int64_t dmoe_forward_ws_offset(const dmoe_layer_desc* desc, int32_t which);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMOE_H */

@@ -1,0 +1,146 @@
+"""End-to-end parity of dmoe_forward against the CPU oracle on workloads the
+oracle finishes in seconds: the tiny layer at full size, and reduced versions
+of the decode, prefill, EP-share and non-divisible layers that still span
+several tiles with ragged tails (GPU)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (DEV, LOGIT_TOL, W_TOL, bf16_values, build_layer, compare_y, layer_inputs, near_tie_tokens, say,
+                      to_dev_bf16, weights_provider)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": synth.config(0),
+    "decode_small": synth.LayerConfig("decode_small", T=64, H=1024, F=384, F_s=384, E=64, E_loc=64, e0=0, K=8,
+                                      dtype="bf16", T_s=64, logits="router"),
+    "prefill_small_fp8": synth.LayerConfig("prefill_small", T=300, H=1024, F=384, F_s=384, E=16, E_loc=16, e0=0,
+                                           K=4, dtype="fp8", T_s=300, logits="router"),
+    "ep_share_small_fp8": synth.LayerConfig("ep_small", T=600, H=512, F=256, F_s=256, E=64, E_loc=8, e0=0, K=8,
+                                            dtype="fp8", T_s=75, logits="zipf"),
+    "ep_share_mid_fp8": synth.LayerConfig("ep_mid", T=600, H=512, F=256, F_s=256, E=64, E_loc=8, e0=24, K=8,
+                                          dtype="fp8", T_s=75, logits="zipf"),
+    "nondiv_small_fp8": synth.LayerConfig("nondiv_small", T=128, H=1024, F=1400, F_s=1400, E=16, E_loc=16, e0=0,
+                                          K=4, dtype="fp8", T_s=128, logits="uniform"),
+    "nondiv_small_bf16": synth.LayerConfig("nondiv_bf16", T=90, H=640, F=200, F_s=136, E=12, E_loc=12, e0=0, K=3,
+                                           dtype="bf16", T_s=50, logits="uniform"),
+    "single_token_fp8": synth.LayerConfig("one_tok", T=1, H=512, F=128, F_s=128, E=16, E_loc=16, e0=0, K=4,
+                                          dtype="fp8", T_s=1, logits="router"),
+}
+
+
+def _run(name):
+    cfg = CASES[name]
+    say(f"[{name}] {cfg}")
+    layer = build_layer(cfg)
+    x_bits, wr, given = layer_inputs(cfg)
+    x = to_dev_bf16(x_bits)
+    get = weights_provider(cfg)
+    ref = oracle.moe_forward(cfg, x_bits, get, w_r=wr, logits=given)
+    return cfg, layer, x, x_bits, wr, given, ref
+
+
+def _check_given_logits_path(cfg, layer, x, ref, logits_np):
+    """Same logits on both sides: routing, permutation and x codes must be bit-exact."""
+    out = layer.forward(x, cfg.T_s, logits=torch.from_numpy(logits_np).to(DEV))
+    torch.cuda.synchronize()
+    d, p, ws = out["_call"]
+    np.testing.assert_array_equal(out["topk_ids"].cpu().numpy(), ref.ids)
+    assert np.max(np.abs(out["topk_w"].cpu().numpy().astype(np.float64) - ref.w)) <= W_TOL
+    off_r, rt_r, rs_r, tr_r = oracle.permute(ref.ids, cfg.e0, cfg.E_loc)
+    M = int(off_r[-1])
+    np.testing.assert_array_equal(layer.ws_view(d, ws, "offsets").cpu().numpy(), off_r)
+    np.testing.assert_array_equal(layer.ws_view(d, ws, "row_token").cpu().numpy()[:M], rt_r)
+    np.testing.assert_array_equal(layer.ws_view(d, ws, "row_slot").cpu().numpy()[:M], rs_r)
+    np.testing.assert_array_equal(layer.ws_view(d, ws, "token_row").cpu().numpy(), tr_r)
+    if cfg.dtype == "fp8":
+        np.testing.assert_array_equal(layer.ws_view(d, ws, "x_codes").cpu().numpy(), ref.x_codes)
+        np.testing.assert_array_equal(layer.ws_view(d, ws, "x_scales").cpu().numpy(), ref.x_scales)
+    y = bf16_values(out["y"])
+    # rows with no local pair and no shared expert are exactly zero on both sides
+    idle = ~np.any(tr_r >= 0, axis=1) & (np.arange(cfg.T) >= cfg.T_s)
+    assert np.all(y[idle] == 0) and np.all(ref.y[idle] == 0)
+    compare_y(y[~idle], ref.y[~idle], "y (given logits)")
+    return out
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_matches_oracle(name):
+    cfg, layer, x, x_bits, wr, given, ref = _run(name)
+    if given is not None:
+        _check_given_logits_path(cfg, layer, x, ref, given)
+        return
+    # 1) the oracle's logits given to the GPU: exact routing, tolerance on y
+    _check_given_logits_path(cfg, layer, x, ref, ref.logits)
+    # 2) the full path with the GPU's own router logits
+    out = layer.forward(x, cfg.T_s, w_router=torch.from_numpy(wr).to(DEV))
+    torch.cuda.synchronize()
+    L = out["logits"].cpu().numpy()
+    err = float(np.max(np.abs(L.astype(np.float64) - ref.logits)))
+    say(f"  router logits max |dL| = {err:.3e}")
+    assert err <= LOGIT_TOL
+    ids = out["topk_ids"].cpu().numpy()
+    diff = near_tie_tokens(ids, ref.ids, ref.logits, 2 * LOGIT_TOL)
+    keep = np.setdiff1d(np.arange(cfg.T), diff)
+    assert diff.size <= max(1, cfg.T // 100), f"{diff.size} tokens routed differently"
+    compare_y(bf16_values(out["y"])[keep], ref.y[keep], "y (own logits)")
+
+
+def test_forward_is_deterministic():
+    cfg, layer, x, x_bits, wr, given, ref = _run("prefill_small_fp8")
+    wdev = torch.from_numpy(wr).to(DEV)
+    a = layer.forward(x, cfg.T_s, w_router=wdev)["y"].clone()
+    b = layer.forward(x, cfg.T_s, w_router=wdev)["y"].clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_all_tokens_on_one_expert_and_empty_experts():
+    """Every token's top-1 is expert 5; most experts get no rows at all."""
+    cfg = synth.LayerConfig("skew", T=200, H=512, F=256, F_s=256, E=32, E_loc=32, e0=0, K=2, dtype="fp8",
+                            T_s=0, logits="uniform")
+    layer = build_layer(cfg)
+    x_bits = synth.x_bf16(cfg)
+    L = np.full((cfg.T, cfg.E), -5.0, np.float32)
+    L[:, 5] = 3.0
+    L[:, 9] = np.linspace(-1, 1, cfg.T).astype(np.float32)
+    ref = oracle.moe_forward(cfg, x_bits, weights_provider(cfg), logits=L)
+    _check_given_logits_path(cfg, layer, to_dev_bf16(x_bits), ref, L)
+
+
+def test_zero_tokens_is_a_no_op():
+    cfg = CASES["tiny"]
+    layer = build_layer(cfg)
+    x = torch.empty((0, cfg.H), dtype=torch.bfloat16, device=DEV)
+    out = layer.forward(x, 0, logits=torch.empty((0, cfg.E), dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    assert out["y"].shape == (0, cfg.H)
+
+
+def test_separate_entry_points_match_forward():
+    """route -> permute -> quant -> gateup -> quant -> down -> shared -> combine, one call at a time."""
+    import fp8_expert_ffn_amd as dm
+    cfg, layer, x, x_bits, wr, given, ref = _run("nondiv_small_fp8")
+    full = layer.forward(x, cfg.T_s, logits=torch.from_numpy(given).to(DEV))["y"].clone()
+    ids, w = dm.dmoe_route(torch.from_numpy(given).to(DEV), cfg.K)
+    off, rt, rs, tr = dm.dmoe_permute(ids, cfg.e0, cfg.E_loc)
+    xq, xs = dm.dmoe_quant_act(x)
+    mcap = cfg.T * cfg.K
+    h = torch.empty((mcap, layer.fpad), dtype=torch.bfloat16, device=DEV)
+    dm.dmoe_grouped_gemm_gateup(dm.DMOE_FP8_E4M3, xq, xs, rt, off, cfg.E_loc, mcap, layer.w_gate, layer.w_up,
+                                layer.s_gate, layer.s_up, cfg.H, cfg.F, h)
+    M = int(off[-1].item())
+    hq, hs = dm.dmoe_quant_act(h[:M], cfg.F)
+    o = torch.empty((mcap, cfg.H), dtype=torch.bfloat16, device=DEV)
+    dm.dmoe_grouped_gemm_down(dm.DMOE_FP8_E4M3, hq, hs, off, cfg.E_loc, M, layer.w_down, layer.s_down, cfg.F,
+                              cfg.H, o)
+    s = torch.empty((cfg.T_s, cfg.H), dtype=torch.bfloat16, device=DEV)
+    dm.dmoe_shared_expert(dm.DMOE_FP8_E4M3, xq, xs, cfg.T_s, layer.sw_gate, layer.sw_up, layer.sw_down,
+                          (layer.ss_gate, layer.ss_up, layer.ss_down), cfg.H, cfg.F_s, s)
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=DEV)
+    dm.dmoe_combine(o, tr, w, s, cfg.T_s, cfg.H, y)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), full.view(torch.int16))

@@ -1,0 +1,97 @@
+"""libdmoe on the host (no GPU): the library loads, exports every entry point
+include/dmoe.h declares, and rejects invalid arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dmoe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dmoe_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import fp8_expert_ffn_amd as dm
+    return dm
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("dmoe_route", "dmoe_permute", "dmoe_quant_act", "dmoe_grouped_gemm_gateup", "dmoe_grouped_gemm_down",
+              "dmoe_shared_expert", "dmoe_combine", "dmoe_forward", "dmoe_router_logits"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = L.lib()
+    for n in _declared():
+        assert hasattr(lib, n), f"{n} declared in dmoe.h but not exported"
+    assert set(_declared()) <= set(L._lib.EXPORTS) | {"dmoe_last_error", "dmoe_abi_version"}
+    assert lib.dmoe_abi_version() == 1
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_route_rejects_bad_sizes(L):
+    lib = L.lib()
+    fake = 0x1000
+    assert lib.dmoe_route(fake, 4, 256, 300, fake, fake, None) == L._lib.DMOE_ERR_INVALID_ARG
+    assert b"K = 300" in lib.dmoe_last_error()
+    assert lib.dmoe_route(fake, 4, 2000, 8, fake, fake, None) == L._lib.DMOE_ERR_INVALID_ARG
+    assert lib.dmoe_route(None, 4, 256, 8, fake, fake, None) == L._lib.DMOE_ERR_INVALID_ARG
+    assert lib.dmoe_route(None, 0, 256, 8, None, None, None) == 0  # T == 0 is a no-op
+
+
+def test_quant_act_rejects_misaligned_and_short_pitches(L):
+    lib = L.lib()
+    assert lib.dmoe_quant_act(0x1008, 4, 128, 128, 0x2000, 128, 0x3000, 1, None) == L._lib.DMOE_ERR_ALIGNMENT
+    assert lib.dmoe_quant_act(0x1000, 4, 1400, 1400, 0x2000, 1400, 0x3000, 11, None) == L._lib.DMOE_ERR_INVALID_ARG
+    assert lib.dmoe_quant_act(0x1000, 4, 100, 104, 0x2000, 128, 0x3000, 1, None) == L._lib.DMOE_ERR_INVALID_ARG
+
+
+def test_permute_rejects_small_workspace(L):
+    lib = L.lib()
+    need = lib.dmoe_permute_ws_bytes(64, 8, 256)
+    assert need > 0
+    st = lib.dmoe_permute(0x1000, 64, 8, 0, 256, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, need - 1, None)
+    assert st == L._lib.DMOE_ERR_WORKSPACE
+
+
+def test_gemm_rejects_bad_dtype_and_shapes(L):
+    lib = L.lib()
+    f = 0x1000
+    args = [f, 5120, f, 40, f, f, 256, 512, f, f, 5120, f, f, 5120, 1536, f, 1536, f, 1 << 20, None]
+    assert lib.dmoe_grouped_gemm_gateup(7, *args) == L._lib.DMOE_ERR_UNSUPPORTED
+    bad_h = list(args)
+    bad_h[13] = 5000  # H not a multiple of 128
+    assert lib.dmoe_grouped_gemm_gateup(1, *bad_h) == L._lib.DMOE_ERR_INVALID_ARG
+    small_ws = list(args)
+    small_ws[18] = 16
+    assert lib.dmoe_grouped_gemm_gateup(2, *small_ws) == L._lib.DMOE_ERR_WORKSPACE
+
+
+def test_forward_desc_validation_and_sizes(L):
+    d = L.LayerDesc(8192, 5120, 1536, 1536, 256, 256, 0, 8, 8192, 2, 0)
+    n = L.dmoe_forward_ws_bytes(d)
+    # o [M, H] BF16 dominates: at least T*K*H*2 bytes
+    assert n >= 8192 * 8 * 5120 * 2
+    assert L.dmoe_forward_ws_offset(d, 0) == 0
+    bad = L.LayerDesc(64, 5120, 1536, 1536, 256, 32, 240, 8, 64, 1, 0)  # local experts past E
+    assert L.dmoe_forward_ws_bytes(bad) == 0
+    lib = L.lib()
+    st = lib.dmoe_forward(ctypes.byref(bad), None, None, 0, None)
+    assert st == L._lib.DMOE_ERR_INVALID_ARG
+    assert b"local experts" in lib.dmoe_last_error()
+    bf = L.LayerDesc(64, 5120, 1536, 1536, 256, 256, 0, 8, 64, 1, 0)
+    assert L.dmoe_forward_ws_offset(bf, 4) == -1  # no FP8 codes on the BF16 path
+    ptrs = L.LayerPtrs()
+    st = lib.dmoe_forward(ctypes.byref(bf), ctypes.byref(ptrs), None, 0, None)
+    assert st == L._lib.DMOE_ERR_INVALID_ARG  # x is NULL; rejected before any launch
