@@ -13,7 +13,7 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdmoe.so")
+LIB_PATH = os.environ.get("DMOE_LIB") or os.path.join(HERE, "libdmoe.so")
 
 DMOE_OK = 0
 DMOE_ERR_INVALID_ARG = 1

@@ -53,21 +53,25 @@ def _run(cmd: list[str], verbose: bool) -> None:
         print("\n".join(lines), flush=True)
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source and link libdmoe.so; returns the library path."""
+def build(verbose: bool = False, jobs: int | None = None, out: str | None = None, objdir: str | None = None,
+          extra_flags: list[str] | None = None) -> str:
+    """Compile every source and link libdmoe.so (or `out`); returns the library path."""
     cc = hipcc()
-    os.makedirs(OBJDIR, exist_ok=True)
+    objdir = objdir or OBJDIR
+    lib = out or LIB
+    os.makedirs(objdir, exist_ok=True)
     srcs = sources()
-    objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    flags = HIPCC_FLAGS + list(extra_flags or [])
     jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1, 8))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, [cc, *HIPCC_FLAGS, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
+        futs = [ex.submit(_run, [cc, *flags, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -182,6 +182,7 @@ static dmoe_status check_gemm_common(int dtype, const void* a, int64_t lda, cons
     REQ_PTR(a_scales, "a_scales");
     REQ_PTR(ws0, "weight scales");
     REQ(ldas >= ceil_div(Kdim, 128), DMOE_ERR_INVALID_ARG, "ldas below ceil(K/128)");
+    REQ(Kdim <= 16384, DMOE_ERR_UNSUPPORTED, "FP8 reduction length %d above 16384", Kdim);
   }
   REQ(ws != nullptr && ws_bytes >= gemm_ws_bytes(max_rows, E_loc), DMOE_ERR_WORKSPACE,
       "gemm workspace needs %zu bytes, got %zu", gemm_ws_bytes(max_rows, E_loc), ws_bytes);
@@ -354,10 +355,17 @@ struct FwdLayout {
   int64_t total;
 };
 
+// The shared expert joins the routed GEMM launches as one extra group when its
+// width equals the routed width; its rows then follow the T*K routed rows in h and o.
+bool fuse_shared(const dmoe_layer_desc* d) { return d->T_s > 0 && d->F_s > 0 && d->F_s == d->F; }
+
 FwdLayout fwd_layout(const dmoe_layer_desc* d) {
   FwdLayout L;
   const bool fp8 = d->dtype == DMOE_FP8_E4M3;
+  const bool shared = d->T_s > 0 && d->F_s > 0;
+  const bool fused = fuse_shared(d);
   const int64_t mcap = (int64_t)d->T * d->K;
+  const int64_t rows = mcap + (fused ? d->T_s : 0);
   const int64_t fpad = round_up(d->F, 128);
   const int64_t sizes[W_COUNT] = {
       (int64_t)(d->E_loc + 1) * 4,
@@ -366,14 +374,14 @@ FwdLayout fwd_layout(const dmoe_layer_desc* d) {
       mcap * 4,
       fp8 ? (int64_t)d->T * d->H : -1,
       fp8 ? (int64_t)d->T * (d->H / 128) * 4 : -1,
-      mcap * fpad * 2,
-      fp8 ? mcap * fpad : -1,
-      fp8 ? mcap * ceil_div(d->F, 128) * 4 : -1,
-      mcap * d->H * 2,
-      (d->T_s > 0 && d->F_s > 0) ? (int64_t)d->T_s * d->H * 2 : -1,
+      rows * fpad * 2,
+      fp8 ? rows * fpad : -1,
+      fp8 ? rows * ceil_div(d->F, 128) * 4 : -1,
+      rows * d->H * 2,
+      (shared && !fused) ? (int64_t)d->T_s * d->H * 2 : -1,
       (int64_t)permute_ws_bytes(d->T, d->K, d->E_loc),
-      (int64_t)gemm_ws_bytes((int)mcap, d->E_loc),
-      (d->T_s > 0 && d->F_s > 0) ? shared_layout(d->dtype, d->T_s, d->H, d->F_s).total : -1,
+      (int64_t)gemm_ws_bytes((int)mcap, d->E_loc, fused ? d->T_s : 0),
+      (shared && !fused) ? shared_layout(d->dtype, d->T_s, d->H, d->F_s).total : -1,
   };
   int64_t at = 0;
   for (int i = 0; i < W_COUNT; ++i) {
@@ -384,6 +392,7 @@ FwdLayout fwd_layout(const dmoe_layer_desc* d) {
     L.off[i] = at;
     at += round_up(std::max<int64_t>(sizes[i], 1), 256);
   }
+  if (fused) L.off[W_S] = L.off[W_O] + mcap * d->H * 2;  // shared rows of o
   L.total = at;
   return L;
 }
@@ -400,6 +409,8 @@ dmoe_status check_desc(const dmoe_layer_desc* d) {
   REQ(d->E_loc >= 1 && d->e0 >= 0 && d->e0 + d->E_loc <= d->E, DMOE_ERR_INVALID_ARG,
       "local experts [%d, %d) not inside [0, %d)", d->e0, d->e0 + d->E_loc, d->E);
   REQ(d->T_s >= 0 && d->T_s <= d->T, DMOE_ERR_INVALID_ARG, "T_s = %d outside [0, T]", d->T_s);
+  REQ(d->dtype != DMOE_FP8_E4M3 || (d->H <= 16384 && d->F <= 16384 && d->F_s <= 16384), DMOE_ERR_UNSUPPORTED,
+      "FP8 layers support H, F, F_s up to 16384");
   REQ((int64_t)d->T * d->K <= INT32_MAX / 2, DMOE_ERR_INVALID_ARG, "T*K too large");
   return DMOE_OK;
 }
@@ -482,7 +493,10 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
   STEP(launch_permute(p->topk_ids, d->T, d->K, d->e0, d->E_loc, offsets, row_token, row_slot, token_row,
                       at(W_PERM), stream),
        "permute");
-  STEP(launch_schedule(offsets, d->E_loc, mcap, at(W_GEMM), stream), "schedule");
+  const bool fused = fuse_shared(d);
+  const int xrows = fused ? d->T_s : 0;
+  if (!gemm_uses_stream(mcap, d->E_loc))
+    STEP(launch_schedule(offsets, d->E_loc, mcap, xrows, mcap, at(W_GEMM), stream), "schedule");
   STEP(mark(), "event");
 
   const void* a = p->x;
@@ -501,6 +515,15 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
   STEP(mark(), "event");
   GemmArgs g1{d->dtype, a, lda, a_scales, ldas, row_token, offsets, d->E_loc, mcap, p->w_gate, p->w_up,
               p->ldw_gu, p->ws_gate, p->ws_up, d->H, d->F, h, fpad, at(W_GEMM), true};
+  if (fused) {
+    g1.x_rows = xrows;
+    g1.x_row0 = mcap;
+    g1.x_a_base = mcap;  // shared row mcap + t reads token t
+    g1.xw0 = p->sw_gate;
+    g1.xw1 = p->sw_up;
+    g1.xws0 = p->sws_gate;
+    g1.xws1 = p->sws_up;
+  }
   STEP(launch_gemm_gateup(g1, stream), "gateup");
   STEP(mark(), "event");
 
@@ -511,18 +534,25 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
     uint8_t* hq = at(W_HQ);
     float* hs = reinterpret_cast<float*>(at(W_HS));
     ldhs = ceil_div(d->F, 128);
-    STEP(launch_quant_act(h, mcap, d->F, fpad, hq, fpad, hs, ldhs, stream), "quant h");
+    STEP(launch_quant_act(h, mcap + xrows, d->F, fpad, hq, fpad, hs, ldhs, stream), "quant h");
     ha = hq;
     hsc = hs;
   }
   STEP(mark(), "event");
   GemmArgs g2{d->dtype, ha, fpad, hsc, ldhs, nullptr, offsets, d->E_loc, mcap, p->w_down, nullptr, p->ldw_d,
               p->ws_down, nullptr, d->F, d->H, o, d->H, at(W_GEMM), true};
+  if (fused) {
+    g2.x_rows = xrows;
+    g2.x_row0 = mcap;
+    g2.x_a_base = 0;  // h rows are already in the unified row space
+    g2.xw0 = p->sw_down;
+    g2.xws0 = p->sws_down;
+  }
   STEP(launch_gemm_down(g2, stream), "down");
   STEP(mark(), "event");
 
-  const uint16_t* s_out = nullptr;
-  if (shared) {
+  const uint16_t* s_out = fused ? o + (int64_t)mcap * d->H : nullptr;
+  if (shared && !fused) {
     uint16_t* s = reinterpret_cast<uint16_t*>(at(W_S));
     TRY(run_shared(d->dtype, a, lda, a_scales, ldas, d->T_s, p->sw_gate, p->sw_up, p->sw_down, p->ldsw_gu,
                    p->ldsw_d, p->sws_gate, p->sws_up, p->sws_down, d->H, d->F_s, s, d->H, at(W_SHARED), stream));

@@ -54,9 +54,22 @@ struct GemmArgs {
   int64_t ldo;
   void* ws;               // tile schedule (gemm_ws_bytes)
   bool scheduled = false; // true: ws already holds the schedule for these offsets and max_rows
+  // Optional extra group computed in the same launch (the shared expert): rows
+  // [x_row0, x_row0 + x_rows) of the output row space, identity token map
+  // (A row = row - x_a_base), its own weights and scales (same N and K).
+  int x_rows = 0;
+  int x_row0 = 0;
+  int x_a_base = 0;
+  const void* xw0 = nullptr;
+  const void* xw1 = nullptr;
+  const float* xws0 = nullptr;
+  const float* xws1 = nullptr;
 };
-size_t gemm_ws_bytes(int max_rows, int E_loc);
-hipError_t launch_schedule(const int32_t* offsets, int E_loc, int max_rows, void* ws, hipStream_t stream);
+size_t gemm_ws_bytes(int max_rows, int E_loc, int extra_rows = 0);
+hipError_t launch_schedule(const int32_t* offsets, int E_loc, int max_rows, int extra_rows, int extra_row0,
+                           void* ws, hipStream_t stream);
+// true when launch_gemm_* picks the weight-streaming kernel (it needs no tile schedule)
+bool gemm_uses_stream(int max_rows, int E_loc);
 hipError_t launch_gemm_gateup(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_fill_offsets(int32_t* offsets, int rows, hipStream_t stream);

@@ -15,14 +15,16 @@
 // the host-known bound (max_rows / kBM + E_loc tiles) and surplus workgroups
 // exit on the device. A workgroup owns kBM rows x kBNB weight rows and walks K
 // in 128-byte stages (128 FP8 or 64 BF16 elements) through two LDS buffers.
+#include <type_traits>
+
 #include "dmoe_internal.h"
 
 namespace dmoe {
 
-constexpr int kBM = 64;             // rows per tile
-constexpr int kBNB = 128;           // weight rows per tile (gate/up: 64 gate + 64 up)
+constexpr int kBM = 128;            // rows per tile
 constexpr int kKB = 128;            // K bytes per stage
 constexpr int kPitch = kKB + 16;    // LDS row pitch in bytes (padding spreads the banks)
+constexpr int kMaxSlices = 128;     // FP8 tile kernel: at most 128 scale slices along K (K <= 16384)
 
 struct TileArgs {
   const uint8_t* a;
@@ -43,12 +45,59 @@ struct TileArgs {
   int stages;              // K stages of kKB bytes
   uint16_t* out;
   int64_t ldo;
+  int E_loc;
+  int x_rows, x_row0, x_a_base;  // extra (shared-expert) group, see GemmArgs
+  int x_chunk;                   // > 0: group indices >= E_loc are consecutive chunks of x_chunk rows
+  const uint8_t* xw0;
+  const uint8_t* xw1;
+  const float* xws0;
+  const float* xws1;
 };
 
+// Weights, scales and rows of group g: a routed expert (g < E_loc) or the extra group.
+struct GroupView {
+  const uint8_t* w0;
+  const uint8_t* w1;
+  const float* s0;  // block scales of this group, [nNb][nKb]
+  const float* s1;
+  int row_beg, row_end;
+  bool gather;  // A row = row_token[r]; otherwise A row = r - a_base
+  int a_base;
+};
+
+__device__ __forceinline__ GroupView group_view(const TileArgs& p, int g) {
+  GroupView v;
+  if (g < p.E_loc) {
+    v.w0 = p.w0 + g * p.w_expert_b;
+    v.w1 = p.w1 ? p.w1 + g * p.w_expert_b : nullptr;
+    v.s0 = p.ws0 ? p.ws0 + (int64_t)g * p.nNb * p.nKb : nullptr;
+    v.s1 = p.ws1 ? p.ws1 + (int64_t)g * p.nNb * p.nKb : nullptr;
+    v.row_beg = p.offsets[g];
+    v.row_end = p.offsets[g + 1];
+    v.gather = p.row_token != nullptr;
+    v.a_base = 0;
+  } else {
+    v.w0 = p.xw0;
+    v.w1 = p.xw1;
+    v.s0 = p.xws0;
+    v.s1 = p.xws1;
+    v.row_beg = p.x_row0 + (p.x_chunk > 0 ? (g - p.E_loc) * p.x_chunk : 0);
+    v.row_end = p.x_chunk > 0 ? min(p.x_row0 + p.x_rows, v.row_beg + p.x_chunk) : p.x_row0 + p.x_rows;
+    v.gather = false;
+    v.a_base = p.x_a_base;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int64_t a_row(const TileArgs& p, const GroupView& v, int r) {
+  return v.gather ? (int64_t)p.row_token[r] : (int64_t)(r - v.a_base);
+}
+
 // Tiles past `cap` (only possible when the caller's max_rows understates the
-// real row count) are dropped rather than written past the workspace.
+// real row count) are dropped rather than written past the workspace. The
+// extra group's tiles (group index E_loc) follow the routed ones.
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int E_loc, int bm,
-                                                        int cap, int2* __restrict__ tiles,
+                                                        int x_rows, int x_row0, int cap, int2* __restrict__ tiles,
                                                         int32_t* __restrict__ ntiles) {
   __shared__ int32_t start[1025];
   __shared__ int32_t partial[1024];
@@ -77,7 +126,11 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
     for (int k = 0; k < n && run + k < cap; ++k) tiles[run + k] = make_int2(i, r0 + k * bm);
     run += n;
   }
-  if (t == (int)blockDim.x - 1) *ntiles = min(partial[t], cap);
+  const int32_t routed = partial[blockDim.x - 1];
+  const int32_t nx = (x_rows + bm - 1) / bm;
+  for (int k = t; k < nx; k += blockDim.x)
+    if (routed + k < cap) tiles[routed + k] = make_int2(E_loc, x_row0 + k * bm);
+  if (t == (int)blockDim.x - 1) *ntiles = min(routed + nx, cap);
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
@@ -105,210 +158,309 @@ __device__ __forceinline__ void e4m3x16_to_bf16(const i32x4 src, i32x4& lo, i32x
   hi = i32x4{out[4], out[5], out[6], out[7]};
 }
 
-template <int MODE, bool GATEUP>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(const TileArgs p) {
-  constexpr bool kScaled = MODE != kModeBF16;
-  // global bytes per row per stage, and 16-byte chunks per row
-  constexpr int kSrcRow = MODE == kModeFP8X ? 64 : 128;
-  constexpr int kCpr = kSrcRow / 16;
-  constexpr int kChunksA = kBM * kCpr / 256;   // per thread
-  constexpr int kChunksB = kBNB * kCpr / 256;
-  constexpr int kStagesPerSlice = MODE == kModeFP8X ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kBM * kPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kBNB * kPitch];
-  __shared__ float sSa[2][kBM];
+// Tile kernel. A workgroup (4 waves) owns kBM = 128 rows of one group and 128
+// weight rows (gate/up: 64 gate + 64 up rows, i.e. 64 columns of h; down: 128
+// columns of o). Wave (wm, wn) computes rows [64wm, 64wm+64) x 64 weight rows
+// as 4 x 4 MFMA tiles of 16x16. Operands move global -> LDS with direct
+// (asynchronous, register-free) loads through an NS-stage ring; a stage is
+// 128 bytes of every A and weight row (one 128-wide FP8 scale slice, or 64
+// BF16 elements) plus the A rows' activation scales. LDS rows are 128 bytes,
+// 16-byte units XOR-swizzled by (row >> 1) & 7 so that the 16 rows a fragment
+// read touches hit distinct banks. Grid: 1-D, tile-major, column block fastest.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-  const int tile = blockIdx.x;
+// s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Asynchronous global -> LDS copies of 16 (or 4) bytes per lane: lane l writes
+// LDS bytes [base + 16 l, +16) (resp. [base + 4 l, +4)); base is wave-uniform
+// and goes through M0. Issued from asm so that the compiler's wait insertion,
+// which cannot tell the pipeline's LDS buffers apart, does not make every LDS
+// read wait for every copy in flight; the pipeline waits on vmcnt itself. The
+// instruction writes no register, so nothing of it is live after issue.
+__device__ __forceinline__ void lds_copy16(const void* gptr, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const void* gptr, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(m0) : "memory", "m0");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose release
+// half would wait for every outstanding global load, including the younger
+// pipeline stages). Callers order memory with explicit s_waitcnt first; the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Wave-uniform copy of a pointer (lets the compiler use scalar loads through it).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
+#ifndef DMOE_TILE_NS
+#define DMOE_TILE_NS 2
+#endif
+#ifndef DMOE_TILE_WAVES_PER_EU
+#define DMOE_TILE_WAVES_PER_EU 2
+#endif
+
+template <int MODE, bool GATEUP, int NS>
+__global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(const TileArgs p, int nNB) {
+  constexpr bool kScaled = MODE != kModeBF16;
+  constexpr int MT = 4, NT = 4, NH = 2;
+  constexpr int kRows = kBM + 128;  // A rows, then weight rows
+  static_assert(NS >= 2 && NS <= 4, "pipeline depth");
+  // One LDS variable per stage so the compiler can tell the stages apart (its
+  // wait insertion then lets the younger stages' loads stay in flight).
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kRows * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kRows * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[NS > 2 ? kRows * 128 : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds3[NS > 3 ? kRows * 128 : 16];
+  __shared__ __attribute__((aligned(256))) float lsa0[kBM];
+  __shared__ __attribute__((aligned(256))) float lsa1[kBM];
+  __shared__ __attribute__((aligned(256))) float lsa2[NS > 2 ? kBM : 4];
+  __shared__ __attribute__((aligned(256))) float lsa3[NS > 3 ? kBM : 4];
+  auto stage_ptr = [&](auto uc) -> uint8_t* {
+    constexpr int u = decltype(uc)::value;
+    if constexpr (u == 0) return lds0;
+    else if constexpr (u == 1) return lds1;
+    else if constexpr (u == 2) return lds2;
+    else return lds3;
+  };
+  auto scale_ptr = [&](auto uc) -> float* {
+    constexpr int u = decltype(uc)::value;
+    if constexpr (u == 0) return lsa0;
+    else if constexpr (u == 1) return lsa1;
+    else if constexpr (u == 2) return lsa2;
+    else return lsa3;
+  };
+
+  const int L = blockIdx.x;
+  const int tile = L / nNB, nb = L - tile * nNB;
   if (tile >= *p.ntiles) return;
   const int2 te = p.tiles[tile];
   const int e = te.x, m0 = te.y;
-  const int m_end = p.offsets[e + 1];
-  const int nb = blockIdx.y;
+  const GroupView gv = group_view(p, e);
+  const int m_end = gv.row_end;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-
-  // ---- global source pointers for this thread's chunks ----
-  const uint8_t* srcA[kChunksA];
-  bool okA[kChunksA];
-#pragma unroll
-  for (int i = 0; i < kChunksA; ++i) {
-    const int c = tid + 256 * i;
-    const int m = m0 + c / kCpr;
-    okA[i] = m < m_end;
-    int64_t src = m;
-    if (okA[i] && p.row_token) src = p.row_token[m];
-    srcA[i] = p.a + (okA[i] ? src : 0) * p.lda_b + (c % kCpr) * 16;
-  }
-  const uint8_t* srcB[kChunksB];
-#pragma unroll
-  for (int i = 0; i < kChunksB; ++i) {
-    const int c = tid + 256 * i;
-    const int br = c / kCpr;
-    const uint8_t* base;
-    int64_t row;
-    if (GATEUP) {
-      base = br < 64 ? p.w0 : p.w1;
-      row = (int64_t)nb * 64 + (br & 63);
-    } else {
-      base = p.w0;
-      row = (int64_t)nb * 128 + br;
-    }
-    srcB[i] = base + e * p.w_expert_b + row * p.ldw_b + (c % kCpr) * 16;
-  }
-  int64_t saRow = -1;
-  if (kScaled && tid < kBM) {
-    const int m = m0 + tid;
-    if (m < m_end) saRow = p.row_token ? p.row_token[m] : m;
-  }
-  const int nblk = GATEUP ? (nb >> 1) : nb;  // 128-row weight block of this tile
-  const float* sw0 = kScaled ? p.ws0 + ((int64_t)e * p.nNb + nblk) * p.nKb : nullptr;
-  const float* sw1 = (kScaled && GATEUP) ? p.ws1 + ((int64_t)e * p.nNb + nblk) * p.nKb : nullptr;
-
-  i32x4 ra[kChunksA], rb[kChunksB];
-  float rsa = 0.f;
-  auto load_stage = [&](int s) {
-    const int64_t off = (int64_t)s * kSrcRow;
-#pragma unroll
-    for (int i = 0; i < kChunksA; ++i)
-      ra[i] = okA[i] ? *reinterpret_cast<const i32x4*>(srcA[i] + off) : i32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < kChunksB; ++i) rb[i] = *reinterpret_cast<const i32x4*>(srcB[i] + off);
-    if (kScaled && tid < kBM) rsa = saRow >= 0 ? p.a_scales[saRow * p.ldas + s / kStagesPerSlice] : 0.f;
-  };
-  auto store_chunk = [&](uint8_t* base, int c, const i32x4 v) {
-    if constexpr (MODE == kModeFP8X) {
-      i32x4 lo, hi;
-      e4m3x16_to_bf16(v, lo, hi);
-      uint8_t* d = base + (c / kCpr) * kPitch + (c % kCpr) * 32;
-      *reinterpret_cast<i32x4*>(d) = lo;
-      *reinterpret_cast<i32x4*>(d + 16) = hi;
-    } else {
-      *reinterpret_cast<i32x4*>(base + (c / kCpr) * kPitch + (c % kCpr) * 16) = v;
-    }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kChunksA; ++i) store_chunk(sA[buf], tid + 256 * i, ra[i]);
-#pragma unroll
-    for (int i = 0; i < kChunksB; ++i) store_chunk(sB[buf], tid + 256 * i, rb[i]);
-    if (kScaled && tid < kBM) sSa[buf][tid] = rsa;
-  };
-
-  f32x4 acc[2][4], part[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   const int r16 = lane & 15, g4 = lane >> 4;
-  int browj[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    browj[j] = GATEUP ? ((j < 2 ? 0 : 64) + 32 * wn + 16 * (j & 1)) : (64 * wn + 16 * j);
+  const int ncol0 = GATEUP ? nb * 64 : nb * 128;  // first h / o column of the workgroup
 
-  load_stage(0);
-  store_stage(0);
+  // Direct-load sources: instruction i of this wave fills LDS rows 8*(4i+wave) .. +7,
+  // lane -> row 8*(4i+wave) + lane/8, 16-byte position lane%8.
+  int64_t srcA[4];
+  const uint8_t* srcB[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (4 * i + wave) + (lane >> 3);
+    const int m = m0 + row;
+    const int64_t arow = a_row(p, gv, m < m_end ? m : m0);  // rows past the group reuse a valid row
+    srcA[i] = arow * p.lda_b + 16 * swz(row, lane & 7);
+    int64_t wrow;
+    const uint8_t* base;
+    if (GATEUP) {
+      wrow = ncol0 + (row & 63);
+      base = row < 64 ? gv.w0 : gv.w1;
+    } else {
+      wrow = ncol0 + row;
+      base = gv.w0;
+    }
+    srcB[i] = base + wrow * p.ldw_b + 16 * swz(row, lane & 7);
+  }
+  int64_t srcS = 0;  // waves 0 and 1 load the activation scales of rows 64*wave + lane
+  if (kScaled && wave < 2) {
+    const int m = m0 + 64 * wave + lane;
+    srcS = a_row(p, gv, m < m_end ? m : m0) * p.ldas;
+  }
+  // Weight block scales of the workgroup's columns (one 128-row block; gate and
+  // up for gate/up), staged in LDS before the pipeline starts.
+  __shared__ float lsw[2][kMaxSlices];
+  if constexpr (kScaled) {
+    const int64_t blk = (int64_t)(ncol0 >> 7) * p.nKb;
+    for (int i = tid; i < p.nKb; i += 256) {
+      lsw[0][i] = gv.s0[blk + i];
+      if (GATEUP) lsw[1][i] = gv.s1[blk + i];
+    }
+  }
   __syncthreads();
-  for (int s = 0; s < p.stages; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < p.stages) load_stage(s + 1);
-    // ---- fragments: 32 bytes of one 128-byte LDS row per lane ----
-    i32x4 fa[2][2], fb[4][2];
+
+  auto issue = [&](auto uc, int s) {
+    uint8_t* st = stage_ptr(uc);
+    const int64_t off = (int64_t)s * 128;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint8_t* ptr = &sA[buf][(32 * wm + 16 * i + r16) * kPitch + g4 * 32];
-      fa[i][0] = *reinterpret_cast<const i32x4*>(ptr);
-      fa[i][1] = *reinterpret_cast<const i32x4*>(ptr + 16);
+    for (int i = 0; i < 4; ++i) lds_copy16(p.a + srcA[i] + off, st + (8 * (4 * i + wave)) * 128);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_copy16(srcB[i] + off, st + (kBM + 8 * (4 * i + wave)) * 128);
+    if (kScaled && wave < 2) lds_copy4(p.a_scales + srcS + s, scale_ptr(uc) + 64 * wave);
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // B rows (within the weight region) of this lane's subtiles
+  int brow[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+    brow[j] = GATEUP ? ((j < NH ? 0 : 64) + 32 * wn + 16 * (j % NH) + r16) : (64 * wn + 16 * j + r16);
+
+  auto compute = [&](auto uc, int s) {
+    const uint8_t* st = stage_ptr(uc);
+    const float* lsa = scale_ptr(uc);
+    i32x4 fa[MT][2];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int row = 64 * wm + 16 * i + r16;
+      fa[i][0] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4));
+      fa[i][1] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4 + 1));
     }
+    // a_scale * w_scale of this stage's slice for each of the lane's rows
+    // (index 0: gate or down weights, 1: up weights)
+    float saw[GATEUP ? 2 : 1][MT][4];
+    if constexpr (kScaled) {
+      const float w0s = lsw[0][s];
+      const float w1s = GATEUP ? lsw[1][s] : 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint8_t* ptr = &sB[buf][(browj[j] + r16) * kPitch + g4 * 32];
-      fb[j][0] = *reinterpret_cast<const i32x4*>(ptr);
-      fb[j][1] = *reinterpret_cast<const i32x4*>(ptr + 16);
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = lsa[64 * wm + 16 * i + 4 * g4 + r];
+          saw[0][i][r] = a * w0s;
+          if constexpr (GATEUP) saw[GATEUP ? 1 : 0][i][r] = a * w1s;
+        }
     }
-    if constexpr (MODE == kModeFP8) {
-      const float w0s = sw0[s];
-      const float w1s = GATEUP ? sw1[s] : w0s;
+    if constexpr (MODE == kModeFP8X) {
+      // exact products: codes -> BF16, four 16x16x32 MFMAs per 128-wide slice
+      i32x4 a16[MT][4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        float sa[4];
+      for (int i = 0; i < MT; ++i) {
+        e4m3x16_to_bf16(fa[i][0], a16[i][0], a16[i][1]);
+        e4m3x16_to_bf16(fa[i][1], a16[i][2], a16[i][3]);
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sa[r] = sSa[buf][32 * wm + 16 * i + 4 * g4 + r];
-        const i32x8 a8 = i32x8{fa[i][0][0], fa[i][0][1], fa[i][0][2], fa[i][0][3],
-                               fa[i][1][0], fa[i][1][1], fa[i][1][2], fa[i][1][3]};
+      for (int j = 0; j < NT; ++j) {
+        const int br = kBM + brow[j];
+        const i32x4 b0 = *reinterpret_cast<const i32x4*>(st + br * 128 + 16 * swz(brow[j], 2 * g4));
+        const i32x4 b1 = *reinterpret_cast<const i32x4*>(st + br * 128 + 16 * swz(brow[j], 2 * g4 + 1));
+        i32x4 b16[4];
+        e4m3x16_to_bf16(b0, b16[0], b16[1]);
+        e4m3x16_to_bf16(b1, b16[2], b16[3]);
+        const int wsel = (GATEUP && j >= NH) ? 1 : 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const i32x8 b8 = i32x8{fb[j][0][0], fb[j][0][1], fb[j][0][2], fb[j][0][3],
-                                 fb[j][1][0], fb[j][1][1], fb[j][1][2], fb[j][1][3]};
+        for (int i = 0; i < MT; ++i) {
+          f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4)
+            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a16[i][k4]),
+                                                           __builtin_bit_cast(bf16x8, b16[k4]), part, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[r], saw[wsel][i][r], acc[i][j][r]);
+        }
+      }
+    } else if constexpr (MODE == kModeFP8) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int br = kBM + brow[j];
+        const i32x4 b0 = *reinterpret_cast<const i32x4*>(st + br * 128 + 16 * swz(brow[j], 2 * g4));
+        const i32x4 b1 = *reinterpret_cast<const i32x4*>(st + br * 128 + 16 * swz(brow[j], 2 * g4 + 1));
+        const i32x8 b8 = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        const int wsel = (GATEUP && j >= NH) ? 1 : 0;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const i32x8 a8 = i32x8{fa[i][0][0], fa[i][0][1], fa[i][0][2], fa[i][0][3],
+                                 fa[i][1][0], fa[i][1][1], fa[i][1][2], fa[i][1][3]};
           const f32x4 pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
                                                                              0, 0, 0, 0);
-          const float ws = (GATEUP && j >= 2) ? w1s : w0s;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pr[r], sa[r] * ws, acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pr[r], saw[wsel][i][r], acc[i][j][r]);
         }
       }
     } else {
-      f32x4(&dst)[2][4] = MODE == kModeBF16 ? acc : part;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const bf16x8 alo = __builtin_bit_cast(bf16x8, fa[i][0]);
-        const bf16x8 ahi = __builtin_bit_cast(bf16x8, fa[i][1]);
+      for (int j = 0; j < NT; ++j) {
+        const int br = kBM + brow[j];
+        const i32x4 b0 = *reinterpret_cast<const i32x4*>(st + br * 128 + 16 * swz(brow[j], 2 * g4));
+        const i32x4 b1 = *reinterpret_cast<const i32x4*>(st + br * 128 + 16 * swz(brow[j], 2 * g4 + 1));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          dst[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, __builtin_bit_cast(bf16x8, fb[j][0]), dst[i][j],
-                                                              0, 0, 0);
-          dst[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, __builtin_bit_cast(bf16x8, fb[j][1]), dst[i][j],
-                                                              0, 0, 0);
-        }
-      }
-      if constexpr (MODE == kModeFP8X) {
-        if ((s & 1) == 1) {  // end of a 128-wide slice: promote with the block scales
-          const int sl = s >> 1;
-          const float w0s = sw0[sl];
-          const float w1s = GATEUP ? sw1[sl] : w0s;
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            float sa[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sa[r] = sSa[buf][32 * wm + 16 * i + 4 * g4 + r];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float ws = (GATEUP && j >= 2) ? w1s : w0s;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                acc[i][j][r] = fmaf(part[i][j][r], sa[r] * ws, acc[i][j][r]);
-                part[i][j][r] = 0.f;
-              }
-            }
-          }
+        for (int i = 0; i < MT; ++i) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[i][0]),
+                                                              __builtin_bit_cast(bf16x8, b0), acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[i][1]),
+                                                              __builtin_bit_cast(bf16x8, b1), acc[i][j], 0, 0, 0);
         }
       }
     }
-    if (s + 1 < p.stages) store_stage(buf ^ 1);
-    __syncthreads();
+  };
+
+  // ---- NS-stage pipeline: stage s lives in buffer s % NS ----
+  const int S = p.stages;
+  const bool scale_wave = kScaled && wave < 2;
+  static_for<0, NS - 1>([&](auto uc) {
+    if (decltype(uc)::value < S) issue(uc, decltype(uc)::value);
+  });
+  for (int s0 = 0; s0 < S; s0 += NS) {
+    static_for<0, NS>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const int s = s0 + u;
+      if (s < S) {
+        if (s + NS - 1 < S) {
+          issue(std::integral_constant<int, (u + NS - 1) % NS>{}, s + NS - 1);
+          // stage s is complete once at most the NS-1 younger stages are in flight
+          if (scale_wave) wait_vmcnt<9 * (NS - 1)>();
+          else wait_vmcnt<8 * (NS - 1)>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        stage_barrier();  // every wave's loads of stage s have landed in LDS
+        compute(uc, s);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
+        stage_barrier();  // buffer u may be refilled
+      }
+    });
   }
 
   // ---- epilogue: lane holds rows 4*g4 + r, column r16 of each 16x16 tile ----
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < MT; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 32 * wm + 16 * i + 4 * g4 + r;
+      const int m = m0 + 64 * wm + 16 * i + 4 * g4 + r;
       if (m >= m_end) continue;
       uint16_t* orow = p.out + (int64_t)m * p.ldo;
       if (GATEUP) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = nb * 64 + 32 * wn + 16 * j + r16;
-          const float h = silu(acc[i][j][r]) * acc[i][j + 2][r];
-          orow[col] = (uint16_t)f32_to_bf16(h);
+        for (int j = 0; j < NH; ++j) {
+          const float h = silu(acc[i][j][r]) * acc[i][j + NH][r];
+          orow[ncol0 + 32 * wn + 16 * j + r16] = (uint16_t)f32_to_bf16(h);
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = nb * 128 + 64 * wn + 16 * j + r16;
-          orow[col] = (uint16_t)f32_to_bf16(acc[i][j][r]);
-        }
+        for (int j = 0; j < NT; ++j) orow[ncol0 + 64 * wn + 16 * j + r16] = (uint16_t)f32_to_bf16(acc[i][j][r]);
       }
     }
   }
@@ -329,18 +481,19 @@ constexpr int kRing = 4;
 template <int DT, bool GATEUP, int R>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(const TileArgs p, int n_cols) {
   const int e = blockIdx.y;
-  const int row_beg = p.offsets[e], row_end = p.offsets[e + 1];
+  const GroupView gv = group_view(p, e);
+  const int row_beg = gv.row_beg, row_end = gv.row_end;
   if (row_beg >= row_end) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int n0 = (blockIdx.x * 4 + wave) * 16;
   if (n0 >= n_cols) return;
   const int64_t wcol = g4 * 32;
-  const uint8_t* wg = p.w0 + e * p.w_expert_b + (int64_t)(n0 + r16) * p.ldw_b + wcol;
-  const uint8_t* wu = GATEUP ? p.w1 + e * p.w_expert_b + (int64_t)(n0 + r16) * p.ldw_b + wcol : nullptr;
+  const uint8_t* wg = gv.w0 + (int64_t)(n0 + r16) * p.ldw_b + wcol;
+  const uint8_t* wu = GATEUP ? gv.w1 + (int64_t)(n0 + r16) * p.ldw_b + wcol : nullptr;
   const int nblk = n0 >> 7;
-  const float* sw0 = DT == DMOE_FP8_E4M3 ? p.ws0 + ((int64_t)e * p.nNb + nblk) * p.nKb : nullptr;
-  const float* sw1 = (DT == DMOE_FP8_E4M3 && GATEUP) ? p.ws1 + ((int64_t)e * p.nNb + nblk) * p.nKb : nullptr;
+  const float* sw0 = DT == DMOE_FP8_E4M3 ? gv.s0 + (int64_t)nblk * p.nKb : nullptr;
+  const float* sw1 = (DT == DMOE_FP8_E4M3 && GATEUP) ? gv.s1 + (int64_t)nblk * p.nKb : nullptr;
   constexpr int NM = GATEUP ? 2 : 1;  // weight matrices per wave
 
   for (int m0 = row_beg; m0 < row_end; m0 += 16 * R) {
@@ -351,12 +504,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const TileArgs p, int 
     for (int i = 0; i < R; ++i) {
       const int m = m0 + 16 * i + r16;
       aok[i] = m < row_end;
-      const int64_t src = aok[i] ? (p.row_token ? p.row_token[m] : m) : 0;
+      const int64_t src = aok[i] ? a_row(p, gv, m) : 0;
       arow[i] = p.a + src * p.lda_b + wcol;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int mq = m0 + 16 * i + 4 * g4 + q;
-        srow[i][q] = mq < row_end ? (p.row_token ? p.row_token[mq] : mq) : -1;
+        srow[i][q] = mq < row_end ? a_row(p, gv, mq) : -1;
       }
     }
     f32x4 acc[NM][R];
@@ -480,10 +633,12 @@ hipError_t launch_fill_offsets(int32_t* offsets, int rows, hipStream_t stream) {
   return hipGetLastError();
 }
 
-static int tile_cap(int max_rows, int E_loc) { return (int)ceil_div(max_rows, kBM) + E_loc; }
+static int tile_cap(int max_rows, int E_loc, int extra_rows) {
+  return (int)(ceil_div(max_rows, kBM) + E_loc + ceil_div(extra_rows, kBM));
+}
 
-size_t gemm_ws_bytes(int max_rows, int E_loc) {
-  return (size_t)round_up((int64_t)tile_cap(max_rows, E_loc) * 8, 256) + 256;
+size_t gemm_ws_bytes(int max_rows, int E_loc, int extra_rows) {
+  return (size_t)round_up((int64_t)tile_cap(max_rows, E_loc, extra_rows) * 8, 256) + 256;
 }
 
 static int2* sched_tiles(void* ws) { return static_cast<int2*>(ws); }
@@ -491,16 +646,22 @@ static int32_t* sched_count(void* ws, int cap) {
   return reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + round_up((int64_t)cap * 8, 256));
 }
 
-hipError_t launch_schedule(const int32_t* offsets, int E_loc, int max_rows, void* ws, hipStream_t stream) {
-  const int cap = tile_cap(max_rows, E_loc);
-  schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E_loc, kBM, cap, sched_tiles(ws), sched_count(ws, cap));
+hipError_t launch_schedule(const int32_t* offsets, int E_loc, int max_rows, int extra_rows, int extra_row0,
+                           void* ws, hipStream_t stream) {
+  const int cap = tile_cap(max_rows, E_loc, extra_rows);
+  schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E_loc, kBM, extra_rows, extra_row0, cap, sched_tiles(ws),
+                                          sched_count(ws, cap));
   return hipGetLastError();
 }
 
+bool gemm_uses_stream(int max_rows, int E_loc) { return ceil_div(max_rows, E_loc) <= 32; }
+
 static hipError_t launch_gemm(const GemmArgs& g, bool gateup, hipStream_t stream) {
-  const int cap = tile_cap(g.max_rows, g.E_loc);
-  if (!g.scheduled) {
-    const hipError_t e = launch_schedule(g.offsets, g.E_loc, g.max_rows, g.ws, stream);
+  const int cap = tile_cap(g.max_rows, g.E_loc, g.x_rows);
+  const int64_t per_expert = ceil_div(g.max_rows, g.E_loc);
+  const bool use_stream = gemm_uses_stream(g.max_rows, g.E_loc);
+  if (!g.scheduled && !use_stream) {
+    const hipError_t e = launch_schedule(g.offsets, g.E_loc, g.max_rows, g.x_rows, g.x_row0, g.ws, stream);
     if (e != hipSuccess) return e;
   }
   const int es = g.dtype == DMOE_FP8_E4M3 ? 1 : 2;
@@ -526,14 +687,26 @@ static hipError_t launch_gemm(const GemmArgs& g, bool gateup, hipStream_t stream
   p.stages = (int)(kpad * es / kKB);  // 128-byte stages (the stream kernel and most tile modes)
   p.out = g.out;
   p.ldo = g.ldo;
+  p.E_loc = g.E_loc;
+  p.x_rows = g.x_rows;
+  p.x_row0 = g.x_row0;
+  p.x_a_base = g.x_a_base;
+  p.xw0 = static_cast<const uint8_t*>(g.xw0);
+  p.xw1 = static_cast<const uint8_t*>(g.xw1);
+  p.xws0 = g.xws0;
+  p.xws1 = g.xws1;
+  p.x_chunk = 0;
   // Few rows per expert on average: stream the weights (the tile schedule is not used).
-  const int64_t per_expert = ceil_div(g.max_rows, g.E_loc);
-  if (per_expert <= 32) {
-    const dim3 sgrid((unsigned)(npad / 64), (unsigned)g.E_loc);
+  // The extra group is cut into chunks of 16*R rows, one grid row each.
+  if (use_stream) {
+    const int R = per_expert <= 16 ? 1 : 2;
+    p.x_chunk = 16 * R;
+    const int xchunks = (int)ceil_div(g.x_rows, p.x_chunk);
+    const dim3 sgrid((unsigned)(npad / 64), (unsigned)(g.E_loc + xchunks));
     const int ncols = (int)npad;
 #define DMOE_STREAM(DTV, GU)                                                                         \
   do {                                                                                               \
-    if (per_expert <= 16) gemm_stream_kernel<DTV, GU, 1><<<sgrid, 256, 0, stream>>>(p, ncols);       \
+    if (R == 1) gemm_stream_kernel<DTV, GU, 1><<<sgrid, 256, 0, stream>>>(p, ncols);                 \
     else gemm_stream_kernel<DTV, GU, 2><<<sgrid, 256, 0, stream>>>(p, ncols);                        \
   } while (0)
     if (g.dtype == DMOE_FP8_E4M3) {
@@ -546,15 +719,16 @@ static hipError_t launch_gemm(const GemmArgs& g, bool gateup, hipStream_t stream
 #undef DMOE_STREAM
     return hipGetLastError();
   }
-  // the tile kernel's exact FP8 gate/up mode stages 64 K elements (128 bytes once converted)
-  if (g.dtype == DMOE_FP8_E4M3 && gateup) p.stages = (int)(kpad / 64);
-  const dim3 grid(cap, gateup ? (unsigned)(npad / 64) : (unsigned)(npad / 128));
+  // tile kernel: 128-byte stages for every mode (FP8: one 128-wide slice, BF16: 64 elements)
+  const int nNB = gateup ? (int)(npad / 64) : (int)(npad / 128);
+  const unsigned grid = (unsigned)((int64_t)cap * nNB);
+  constexpr int NS = DMOE_TILE_NS;
   if (g.dtype == DMOE_FP8_E4M3) {
-    if (gateup) gemm_tile_kernel<kModeFP8X, true><<<grid, 256, 0, stream>>>(p);
-    else gemm_tile_kernel<kModeFP8, false><<<grid, 256, 0, stream>>>(p);
+    if (gateup) gemm_tile_kernel<kModeFP8X, true, NS><<<grid, 256, 0, stream>>>(p, nNB);
+    else gemm_tile_kernel<kModeFP8, false, NS><<<grid, 256, 0, stream>>>(p, nNB);
   } else {
-    if (gateup) gemm_tile_kernel<kModeBF16, true><<<grid, 256, 0, stream>>>(p);
-    else gemm_tile_kernel<kModeBF16, false><<<grid, 256, 0, stream>>>(p);
+    if (gateup) gemm_tile_kernel<kModeBF16, true, NS><<<grid, 256, 0, stream>>>(p, nNB);
+    else gemm_tile_kernel<kModeBF16, false, NS><<<grid, 256, 0, stream>>>(p, nNB);
   }
   return hipGetLastError();
 }

@@ -121,6 +121,46 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __r
   }
 }
 
+// All pairs in one block (T*K <= kPermutePairs): masks, counts, offsets and the
+// scatter in a single workgroup.
+__global__ __launch_bounds__(256) void permute_single_kernel(const int32_t* __restrict__ ids, int npairs, int K,
+                                                             int e0, int E_loc, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ row_token,
+                                                             int32_t* __restrict__ row_slot,
+                                                             int32_t* __restrict__ token_row) {
+  extern __shared__ uint32_t smem[];
+  uint32_t* mask = smem;                                          // E_loc * kMaskWords
+  int32_t* base = reinterpret_cast<int32_t*>(smem + E_loc * kMaskWords);  // E_loc
+  __shared__ int32_t partial[256];
+  __shared__ int32_t total;
+  build_masks(ids, 0, npairs, e0, E_loc, mask);
+  for (int e = threadIdx.x; e < E_loc; e += blockDim.x) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kMaskWords; ++w) c += __popc(mask[e * kMaskWords + w]);
+    base[e] = c;
+  }
+  __syncthreads();
+  block_exclusive_scan(base, E_loc, partial, &total);
+  for (int e = threadIdx.x; e < E_loc; e += blockDim.x) offsets[e] = base[e];
+  if (threadIdx.x == 0) offsets[E_loc] = total;
+  for (int pl = threadIdx.x; pl < npairs; pl += blockDim.x) {
+    const int e = ids[pl] - e0;
+    if ((unsigned)e < (unsigned)E_loc) {
+      const uint32_t* m = mask + e * kMaskWords;
+      const int w = pl >> 5;
+      int rank = __popc(m[w] & ((1u << (pl & 31)) - 1u));
+      for (int i = 0; i < w; ++i) rank += __popc(m[i]);
+      const int32_t row = base[e] + rank;
+      row_token[row] = pl / K;
+      row_slot[row] = pl % K;
+      token_row[pl] = row;
+    } else {
+      token_row[pl] = -1;
+    }
+  }
+}
+
 size_t permute_ws_bytes(int T, int K, int E_loc) {
   const int64_t nb = ceil_div((int64_t)T * K, kPermutePairs);
   return (size_t)round_up(std::max<int64_t>(nb, 1) * E_loc * 4, 256);
@@ -133,6 +173,11 @@ hipError_t launch_permute(const int32_t* ids, int T, int K, int e0, int E_loc, i
   const int nb = (int)ceil_div(npairs, kPermutePairs);
   int32_t* counts = static_cast<int32_t*>(ws);
   const size_t lds = (size_t)E_loc * kMaskWords * 4;
+  if (nb == 1 && E_loc <= 512) {
+    permute_single_kernel<<<1, 256, lds + (size_t)E_loc * 4, stream>>>(ids, (int)npairs, K, e0, E_loc, offsets,
+                                                                      row_token, row_slot, token_row);
+    return hipGetLastError();
+  }
   if (nb > 0) permute_count_kernel<<<nb, 256, lds, stream>>>(ids, npairs, e0, E_loc, counts);
   permute_scan_kernel<<<1, 1024, 0, stream>>>(counts, nb, E_loc, offsets);
   if (nb > 0)
