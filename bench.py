@@ -2,6 +2,7 @@
 """MoE-layer throughput of libdmoe on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
+    python bench.py --copy-calibration MIB [--steps REPS]
 
 A step is one dmoe_forward over one batch of synthetic input: router logits
 (or given logits) -> route -> permute -> [quantise x] -> gate/up + SwiGLU ->
@@ -15,6 +16,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import hashlib
 import platform
 import sys
 import time
@@ -46,6 +48,65 @@ def build_layer(cfg, dev):
     return layer
 
 
+def uses_stream_kernel(cfg) -> bool:
+    """The library's choice for the grouped GEMMs: weight streaming when the host bound on rows per local
+    expert, ceil(T*K / E_loc), is at most 32; tile GEMM otherwise."""
+    return -(-cfg.T * cfg.K // cfg.E_loc) <= 32
+
+
+def shared_fused(cfg) -> bool:
+    """The shared expert runs inside the routed launches when it has the routed width."""
+    return cfg.T_s > 0 and cfg.F_s > 0 and cfg.F_s == cfg.F
+
+
+def kernel_files(stream: bool) -> list[str]:
+    csrc = os.path.join(ROOT, "fp8_expert_ffn_amd", "csrc")
+    main = "gemm_stream.hip" if stream else "gemm.hip"
+    return [os.path.join(csrc, f) for f in (main, "gemm_common.h", "dmoe_device.h", "dmoe_internal.h")]
+
+
+def kernel_source_hash(stream: bool) -> str:
+    h = hashlib.sha256()
+    for f in kernel_files(stream):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_record(workload: str, kernel: str, src_hash: str):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (copy-calibrated), from the
+    committed profile summaries; None when no record matches this workload, kernel and kernel source."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    for name in sorted(os.listdir(pdir)):
+        if not name.endswith(".md"):
+            continue
+        with open(os.path.join(pdir, name)) as fh:
+            for line in fh:
+                if not line.startswith("traffic-record: "):
+                    continue
+                rec = json.loads(line[len("traffic-record: "):])
+                if rec.get("workload") == workload and rec.get("kernel") == kernel and \
+                        rec.get("source_sha256") == src_hash:
+                    return rec
+    return None
+
+
+def copy_calibration(mib: int, reps: int) -> int:
+    """A plain device-to-device copy of `mib` MiB, `reps` times: the reference for scaling the HBM counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "reps": reps}), flush=True)
+    return 0
+
+
 def accounting(cfg, offsets: np.ndarray, logits_computed: bool) -> dict:
     """Algorithmic FLOPs and bytes of the layer and of its gate/up launch, on the real routing."""
     es = 1 if cfg.dtype == "fp8" else 2
@@ -64,9 +125,13 @@ def accounting(cfg, offsets: np.ndarray, logits_computed: bool) -> dict:
         flops += 2.0 * T * H * E
     bytes_ = touched * (w_gu + w_d) + ws_gu + ws_d + T * H * 2 + T * H * 2  # weights + x read + y written
     bytes_ += E * H * 4 if logits_computed else T * E * 4                  # router weight or given logits
-    gu_flops = 2.0 * M * 2 * H * F
-    gu_bytes = touched * w_gu + T * H * es + M * F * 2                     # weights + A rows once + h written
-    return dict(M=M, touched=touched, flops=flops, bytes=bytes_, gu_flops=gu_flops, gu_bytes=gu_bytes)
+    # gate/up launch: routed experts, plus the shared expert when it runs as an extra group of that launch
+    a_bytes = T * H * es + (T * nb(H) * 4 if cfg.dtype == "fp8" else 0)     # x (codes + scales) read once
+    gu_rows = M + (Ts if shared_fused(cfg) else 0)
+    gu_flops = 2.0 * gu_rows * 2 * H * F
+    gu_bytes = touched * w_gu + (ws_gu if shared_fused(cfg) else 0) + a_bytes + gu_rows * F * 2  # + h written
+    return dict(M=M, touched=touched, flops=flops, bytes=bytes_, gu_flops=gu_flops, gu_bytes=gu_bytes,
+                gu_rows=gu_rows)
 
 
 def cpu_baseline(cfg, x_bits, wr, given, seconds: float) -> dict:
@@ -106,6 +171,8 @@ def main() -> int:
                                                                 "3 EP share, 4 non-divisible)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the multi-GPU exchange "
@@ -121,6 +188,8 @@ def main() -> int:
         return 2
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration, max(1, args.steps))
     cfg = synth.config(args.workload)
     t0 = time.time()
     layer = build_layer(cfg, dev)
@@ -174,7 +243,14 @@ def main() -> int:
         achieved = acc["gu_flops"] / gu_sec / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TFLOPS[cfg.dtype], 4), "traffic": None}
-    roof["kernel"] = f"gemm_tile_kernel<{cfg.dtype}, gate/up> (routed experts)"
+    stream_k = uses_stream_kernel(cfg)
+    kname = f"{'gemm_stream_kernel' if stream_k else 'gemm_tile_kernel'}<{cfg.dtype}, gate/up>"
+    roof["kernel"] = kname + (" (routed experts + shared expert as an extra group)" if shared_fused(cfg)
+                              else " (routed experts)")
+    rec = traffic_record(cfg.name, kname, kernel_source_hash(stream_k))
+    if rec is not None:
+        roof["traffic"] = rec["hbm_bytes_per_launch"]
+        roof["traffic_source"] = rec["summary"]
     roof["alg_bytes_per_launch"] = acc["gu_bytes"]
     roof["alg_flops_per_launch"] = acc["gu_flops"]
     roof["avg_launch_ms"] = round(stage_ms["gateup"], 5)

@@ -13,85 +13,13 @@
 // Work decomposition: a schedule kernel turns the per-expert row offsets into
 // a list of (expert, first row) tiles of kBM rows; the GEMM grid is sized from
 // the host-known bound (max_rows / kBM + E_loc tiles) and surplus workgroups
-// exit on the device. A workgroup owns kBM rows x kBNB weight rows and walks K
-// in 128-byte stages (128 FP8 or 64 BF16 elements) through two LDS buffers.
+// exit on the device. A workgroup owns kBM rows x (32 * NT) weight rows and
+// walks K in 128-byte stages (128 FP8 or 64 BF16 elements) through an LDS ring.
 #include <type_traits>
 
-#include "dmoe_internal.h"
+#include "gemm_common.h"
 
 namespace dmoe {
-
-constexpr int kBM = 128;            // rows per tile
-constexpr int kKB = 128;            // K bytes per stage
-constexpr int kPitch = kKB + 16;    // LDS row pitch in bytes (padding spreads the banks)
-constexpr int kMaxSlices = 128;     // FP8 tile kernel: at most 128 scale slices along K (K <= 16384)
-
-struct TileArgs {
-  const uint8_t* a;
-  int64_t lda_b;  // bytes
-  const float* a_scales;
-  int64_t ldas;
-  const int32_t* row_token;
-  const int32_t* offsets;
-  const int2* tiles;
-  const int32_t* ntiles;
-  const uint8_t* w0;
-  const uint8_t* w1;
-  int64_t ldw_b;           // bytes
-  int64_t w_expert_b;      // bytes between experts
-  const float* ws0;
-  const float* ws1;
-  int nNb, nKb;            // 128-blocks along N (weight rows) and K
-  int stages;              // K stages of kKB bytes
-  uint16_t* out;
-  int64_t ldo;
-  int E_loc;
-  int x_rows, x_row0, x_a_base;  // extra (shared-expert) group, see GemmArgs
-  int x_chunk;                   // > 0: group indices >= E_loc are consecutive chunks of x_chunk rows
-  const uint8_t* xw0;
-  const uint8_t* xw1;
-  const float* xws0;
-  const float* xws1;
-};
-
-// Weights, scales and rows of group g: a routed expert (g < E_loc) or the extra group.
-struct GroupView {
-  const uint8_t* w0;
-  const uint8_t* w1;
-  const float* s0;  // block scales of this group, [nNb][nKb]
-  const float* s1;
-  int row_beg, row_end;
-  bool gather;  // A row = row_token[r]; otherwise A row = r - a_base
-  int a_base;
-};
-
-__device__ __forceinline__ GroupView group_view(const TileArgs& p, int g) {
-  GroupView v;
-  if (g < p.E_loc) {
-    v.w0 = p.w0 + g * p.w_expert_b;
-    v.w1 = p.w1 ? p.w1 + g * p.w_expert_b : nullptr;
-    v.s0 = p.ws0 ? p.ws0 + (int64_t)g * p.nNb * p.nKb : nullptr;
-    v.s1 = p.ws1 ? p.ws1 + (int64_t)g * p.nNb * p.nKb : nullptr;
-    v.row_beg = p.offsets[g];
-    v.row_end = p.offsets[g + 1];
-    v.gather = p.row_token != nullptr;
-    v.a_base = 0;
-  } else {
-    v.w0 = p.xw0;
-    v.w1 = p.xw1;
-    v.s0 = p.xws0;
-    v.s1 = p.xws1;
-    v.row_beg = p.x_row0 + (p.x_chunk > 0 ? (g - p.E_loc) * p.x_chunk : 0);
-    v.row_end = p.x_chunk > 0 ? min(p.x_row0 + p.x_rows, v.row_beg + p.x_chunk) : p.x_row0 + p.x_rows;
-    v.gather = false;
-    v.a_base = p.x_a_base;
-  }
-  return v;
-}
-
-__device__ __forceinline__ int64_t a_row(const TileArgs& p, const GroupView& v, int r) {
-  return v.gather ? (int64_t)p.row_token[r] : (int64_t)(r - v.a_base);
-}
 
 // Tiles past `cap` (only possible when the caller's max_rows understates the
 // real row count) are dropped rather than written past the workspace. The
@@ -133,41 +61,31 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
   if (t == (int)blockDim.x - 1) *ntiles = min(routed + nx, cap);
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
-
-// Operand modes of the tile kernel. Every mode keeps 128-byte K rows in LDS.
+// Operand modes of the tile kernel. Every mode moves 128-byte K rows through LDS.
 //  kModeBF16: BF16 operands, 64 K per stage, BF16 MFMA.
-//  kModeFP8X: E4M3 operands converted exactly to BF16 on the way into LDS,
-//             64 K per stage (two stages per 128-wide scale slice), BF16 MFMA:
-//             every product and the FP32 accumulation of a slice are exact to
-//             FP32 rounding.
-//  kModeFP8:  E4M3 operands in LDS, 128 K per stage (one scale slice), FP8 MFMA
+//  kModeFP8X: E4M3 operands, 128 K per stage (one scale slice); fragments are
+//             converted exactly to BF16 after the LDS read and multiplied on
+//             BF16 matrix cores: every product is exact and the slice's sum is
+//             accumulated in FP32 before the a_scale * w_scale promotion.
+//  kModeFP8:  E4M3 operands, 128 K per stage (one scale slice), FP8 MFMA
 //             (the matrix core's own accumulation precision within a slice).
 constexpr int kModeBF16 = 0, kModeFP8X = 1, kModeFP8 = 2;
 
-__device__ __forceinline__ void e4m3x16_to_bf16(const i32x4 src, i32x4& lo, i32x4& hi) {
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-  int out[8];
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t v = (uint32_t)src[w];
-    out[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false));
-    out[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true));
-  }
-  lo = i32x4{out[0], out[1], out[2], out[3]};
-  hi = i32x4{out[4], out[5], out[6], out[7]};
-}
-
-// Tile kernel. A workgroup (4 waves) owns kBM = 128 rows of one group and 128
-// weight rows (gate/up: 64 gate + 64 up rows, i.e. 64 columns of h; down: 128
-// columns of o). Wave (wm, wn) computes rows [64wm, 64wm+64) x 64 weight rows
-// as 4 x 4 MFMA tiles of 16x16. Operands move global -> LDS with direct
-// (asynchronous, register-free) loads through an NS-stage ring; a stage is
-// 128 bytes of every A and weight row (one 128-wide FP8 scale slice, or 64
-// BF16 elements) plus the A rows' activation scales. LDS rows are 128 bytes,
-// 16-byte units XOR-swizzled by (row >> 1) & 7 so that the 16 rows a fragment
-// read touches hit distinct banks. Grid: 1-D, tile-major, column block fastest.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+// Tile kernel. A workgroup (4 waves) owns kBM = 128 rows of one group and
+// 32 * NT weight rows (gate/up: 16 * NT gate + 16 * NT up rows, i.e. 16 * NT
+// columns of h; down: 32 * NT columns of o). Wave (wm, wn) computes rows
+// [64 wm, 64 wm + 64) x 16 * NT weight rows as 4 x NT MFMA tiles of 16x16
+// (NT = 4 by default: two workgroups fit one CU). Operands move global -> LDS
+// with direct (asynchronous, register-free) loads through an NS-stage ring; a
+// stage is 128 bytes of every A and weight row (one 128-wide FP8 scale slice,
+// or 64 BF16 elements) plus the A rows' activation scales. LDS rows are 128
+// bytes, 16-byte units XOR-swizzled by (row >> 1) & 7 so that the 16 rows a
+// fragment read touches hit distinct banks. Grid: 1-D, tile-major, column
+// block fastest.
+#ifndef DMOE_SWZ_SHIFT
+#define DMOE_SWZ_SHIFT 1
+#endif
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> DMOE_SWZ_SHIFT) & 7); }
 
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding).
 template <int N>
@@ -225,15 +143,26 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
 #ifndef DMOE_TILE_WAVES_PER_EU
 #define DMOE_TILE_WAVES_PER_EU 2
 #endif
+#ifndef DMOE_TILE_XCD_REMAP
+#define DMOE_TILE_XCD_REMAP 0
+#endif
+#ifndef DMOE_TILE_NT_GATEUP
+#define DMOE_TILE_NT_GATEUP 4
+#endif
+#ifndef DMOE_TILE_NT_DOWN
+#define DMOE_TILE_NT_DOWN 4
+#endif
 
-template <int MODE, bool GATEUP, int NS>
-__global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(const TileArgs p, int nNB) {
+template <int MODE, bool GATEUP, int NS, int NT>
+__global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gemm_tile_kernel(const TileArgs p,
+                                                                                              int nNB, int n_valid) {
   constexpr bool kScaled = MODE != kModeBF16;
-  constexpr int MT = 4, NT = 4, NH = 2;
-  constexpr int kRows = kBM + 128;  // A rows, then weight rows
+  constexpr int MT = 4, NH = NT / 2;   // gate/up: NH gate subtiles, then NH up subtiles per wave
+  constexpr int kRowsB = 32 * NT;      // weight rows per workgroup
+  constexpr int kRows = kBM + kRowsB;  // A rows, then weight rows
+  constexpr int kInstA = kBM / 32, kInstB = kRowsB / 32;  // direct copies per wave per stage
   static_assert(NS >= 2 && NS <= 4, "pipeline depth");
-  // One LDS variable per stage so the compiler can tell the stages apart (its
-  // wait insertion then lets the younger stages' loads stay in flight).
+  // One LDS variable per stage so that each stage is a distinct object.
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kRows * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kRows * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[NS > 2 ? kRows * 128 : 16];
@@ -257,9 +186,28 @@ __global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(
     else return lsa3;
   };
 
+  // The direct copies write LDS from asm that sees only integer M0 bases; hand
+  // the buffers' addresses to an asm statement once so that the compiler
+  // treats them as escaped and every later memory-clobbering asm (the copies,
+  // the barriers) as a possible writer of them.
+  asm volatile("" ::"v"(lds0), "v"(lds1), "v"(lds2), "v"(lds3), "v"(lsa0), "v"(lsa1), "v"(lsa2), "v"(lsa3)
+               : "memory");
+
+#if DMOE_TILE_XCD_REMAP
+  // Workgroups are dealt to the 8 XCDs round robin (XCD = blockIdx % 8); give
+  // each XCD one contiguous range of the real work items (tile-major, column
+  // block fastest) so that a tile's A rows and an expert's weights are fetched
+  // into one XCD's L2 instead of all eight. The grid is a multiple of 8.
+  const int nitems = *p.ntiles * nNB;
+  const int per_xcd = (nitems + 7) >> 3;
+  const int L = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || L >= nitems) return;
+  const int tile = L / nNB, nb = L - tile * nNB;
+#else
   const int L = blockIdx.x;
   const int tile = L / nNB, nb = L - tile * nNB;
   if (tile >= *p.ntiles) return;
+#endif
   const int2 te = p.tiles[tile];
   const int e = te.x, m0 = te.y;
   const GroupView gv = group_view(p, e);
@@ -267,42 +215,54 @@ __global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int ncol0 = GATEUP ? nb * 64 : nb * 128;  // first h / o column of the workgroup
+  // first h (gate/up) or o (down) column of the workgroup and of this wave
+  const int ncol0 = nb * (GATEUP ? 16 * NT : 32 * NT);
+  const int wcol0 = ncol0 + wn * 16 * (GATEUP ? NH : NT);
+  const bool active = GATEUP || wcol0 < n_valid;  // down: waves past N only help with the copies
 
-  // Direct-load sources: instruction i of this wave fills LDS rows 8*(4i+wave) .. +7,
+  // Direct-copy sources: copy i of this wave fills LDS rows 8*(4i+wave) .. +7,
   // lane -> row 8*(4i+wave) + lane/8, 16-byte position lane%8.
-  int64_t srcA[4];
-  const uint8_t* srcB[4];
+  int64_t srcA[kInstA];
+  const uint8_t* srcB[kInstB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kInstA; ++i) {
     const int row = 8 * (4 * i + wave) + (lane >> 3);
     const int m = m0 + row;
     const int64_t arow = a_row(p, gv, m < m_end ? m : m0);  // rows past the group reuse a valid row
     srcA[i] = arow * p.lda_b + 16 * swz(row, lane & 7);
+  }
+#pragma unroll
+  for (int i = 0; i < kInstB; ++i) {
+    const int row = 8 * (4 * i + wave) + (lane >> 3);
     int64_t wrow;
     const uint8_t* base;
     if (GATEUP) {
-      wrow = ncol0 + (row & 63);
-      base = row < 64 ? gv.w0 : gv.w1;
+      wrow = ncol0 + (row % (16 * NT));
+      base = row < 16 * NT ? gv.w0 : gv.w1;
     } else {
-      wrow = ncol0 + row;
+      wrow = ncol0 + row < n_valid ? ncol0 + row : 0;  // rows past N (inactive waves) reread row 0
       base = gv.w0;
     }
     srcB[i] = base + wrow * p.ldw_b + 16 * swz(row, lane & 7);
   }
-  int64_t srcS = 0;  // waves 0 and 1 load the activation scales of rows 64*wave + lane
+  int64_t srcS = 0;  // waves 0 and 1 copy the activation scales of rows 64*wave + lane
   if (kScaled && wave < 2) {
     const int m = m0 + 64 * wave + lane;
     srcS = a_row(p, gv, m < m_end ? m : m0) * p.ldas;
   }
-  // Weight block scales of the workgroup's columns (one 128-row block; gate and
-  // up for gate/up), staged in LDS before the pipeline starts.
+  // Weight block scales staged in LDS before the pipeline starts: gate/up: the
+  // 128-row block of the gate and of the up rows; down: the block of each
+  // column-wave's 16*NT columns.
   __shared__ float lsw[2][kMaxSlices];
   if constexpr (kScaled) {
-    const int64_t blk = (int64_t)(ncol0 >> 7) * p.nKb;
-    for (int i = tid; i < p.nKb; i += 256) {
-      lsw[0][i] = gv.s0[blk + i];
-      if (GATEUP) lsw[1][i] = gv.s1[blk + i];
+    for (int i = tid; i < 2 * p.nKb; i += 256) {
+      const int w = i / p.nKb, sl = i - w * p.nKb;
+      if (GATEUP) {
+        lsw[w][sl] = (w == 0 ? gv.s0 : gv.s1)[(int64_t)(ncol0 >> 7) * p.nKb + sl];
+      } else {
+        const int col = ncol0 + w * 16 * NT;
+        lsw[w][sl] = col < n_valid ? gv.s0[(int64_t)(col >> 7) * p.nKb + sl] : 0.f;
+      }
     }
   }
   __syncthreads();
@@ -311,9 +271,9 @@ __global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(
     uint8_t* st = stage_ptr(uc);
     const int64_t off = (int64_t)s * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_copy16(p.a + srcA[i] + off, st + (8 * (4 * i + wave)) * 128);
+    for (int i = 0; i < kInstA; ++i) lds_copy16(p.a + srcA[i] + off, st + (8 * (4 * i + wave)) * 128);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_copy16(srcB[i] + off, st + (kBM + 8 * (4 * i + wave)) * 128);
+    for (int i = 0; i < kInstB; ++i) lds_copy16(srcB[i] + off, st + (kBM + 8 * (4 * i + wave)) * 128);
     if (kScaled && wave < 2) lds_copy4(p.a_scales + srcS + s, scale_ptr(uc) + 64 * wave);
   };
 
@@ -323,11 +283,11 @@ __global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // B rows (within the weight region) of this lane's subtiles
-  int brow[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-    brow[j] = GATEUP ? ((j < NH ? 0 : 64) + 32 * wn + 16 * (j % NH) + r16) : (64 * wn + 16 * j + r16);
+  // weight rows (within the weight region) of this lane's subtiles
+  auto brow = [&](int j) -> int {
+    if (GATEUP) return (j < NH ? 0 : 16 * NT) + wn * 16 * NH + 16 * (j % NH) + r16;
+    return wn * 16 * NT + 16 * j + r16;
+  };
 
   auto compute = [&](auto uc, int s) {
     const uint8_t* st = stage_ptr(uc);
@@ -343,7 +303,7 @@ __global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(
     // (index 0: gate or down weights, 1: up weights)
     float saw[GATEUP ? 2 : 1][MT][4];
     if constexpr (kScaled) {
-      const float w0s = lsw[0][s];
+      const float w0s = GATEUP ? lsw[0][s] : lsw[wn][s];
       const float w1s = GATEUP ? lsw[1][s] : 0.f;
 #pragma unroll
       for (int i = 0; i < MT; ++i)
@@ -364,9 +324,10 @@ __global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const int br = kBM + brow[j];
-        const i32x4 b0 = *reinterpret_cast<const i32x4*>(st + br * 128 + 16 * swz(brow[j], 2 * g4));
-        const i32x4 b1 = *reinterpret_cast<const i32x4*>(st + br * 128 + 16 * swz(brow[j], 2 * g4 + 1));
+        const int bj = brow(j);
+        const uint8_t* bp = st + (kBM + bj) * 128;
+        const i32x4 b0 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4));
+        const i32x4 b1 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1));
         i32x4 b16[4];
         e4m3x16_to_bf16(b0, b16[0], b16[1]);
         e4m3x16_to_bf16(b1, b16[2], b16[3]);
@@ -385,9 +346,10 @@ __global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(
     } else if constexpr (MODE == kModeFP8) {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const int br = kBM + brow[j];
-        const i32x4 b0 = *reinterpret_cast<const i32x4*>(st + br * 128 + 16 * swz(brow[j], 2 * g4));
-        const i32x4 b1 = *reinterpret_cast<const i32x4*>(st + br * 128 + 16 * swz(brow[j], 2 * g4 + 1));
+        const int bj = brow(j);
+        const uint8_t* bp = st + (kBM + bj) * 128;
+        const i32x4 b0 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4));
+        const i32x4 b1 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1));
         const i32x8 b8 = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
         const int wsel = (GATEUP && j >= NH) ? 1 : 0;
 #pragma unroll
@@ -403,9 +365,10 @@ __global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(
     } else {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const int br = kBM + brow[j];
-        const i32x4 b0 = *reinterpret_cast<const i32x4*>(st + br * 128 + 16 * swz(brow[j], 2 * g4));
-        const i32x4 b1 = *reinterpret_cast<const i32x4*>(st + br * 128 + 16 * swz(brow[j], 2 * g4 + 1));
+        const int bj = brow(j);
+        const uint8_t* bp = st + (kBM + bj) * 128;
+        const i32x4 b0 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4));
+        const i32x4 b1 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1));
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[i][0]),
@@ -418,6 +381,7 @@ __global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(
   };
 
   // ---- NS-stage pipeline: stage s lives in buffer s % NS ----
+  constexpr int kCopies = kInstA + kInstB;  // per wave per stage, plus one scale copy on waves 0 and 1
   const int S = p.stages;
   const bool scale_wave = kScaled && wave < 2;
   static_for<0, NS - 1>([&](auto uc) {
@@ -431,19 +395,20 @@ __global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(
         if (s + NS - 1 < S) {
           issue(std::integral_constant<int, (u + NS - 1) % NS>{}, s + NS - 1);
           // stage s is complete once at most the NS-1 younger stages are in flight
-          if (scale_wave) wait_vmcnt<9 * (NS - 1)>();
-          else wait_vmcnt<8 * (NS - 1)>();
+          if (scale_wave) wait_vmcnt<(kCopies + 1) * (NS - 1)>();
+          else wait_vmcnt<kCopies * (NS - 1)>();
         } else {
           wait_vmcnt<0>();
         }
-        stage_barrier();  // every wave's loads of stage s have landed in LDS
-        compute(uc, s);
+        stage_barrier();  // every wave's copies of stage s have landed in LDS
+        if (active) compute(uc, s);
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
         stage_barrier();  // buffer u may be refilled
       }
     });
   }
 
+  if (!active) return;
   // ---- epilogue: lane holds rows 4*g4 + r, column r16 of each 16x16 tile ----
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
@@ -456,168 +421,11 @@ __global__ __launch_bounds__(256, DMOE_TILE_WAVES_PER_EU) void gemm_tile_kernel(
 #pragma unroll
         for (int j = 0; j < NH; ++j) {
           const float h = silu(acc[i][j][r]) * acc[i][j + NH][r];
-          orow[ncol0 + 32 * wn + 16 * j + r16] = (uint16_t)f32_to_bf16(h);
+          orow[wcol0 + 16 * j + r16] = (uint16_t)f32_to_bf16(h);
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) orow[ncol0 + 64 * wn + 16 * j + r16] = (uint16_t)f32_to_bf16(acc[i][j][r]);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Weight-streaming variant for few rows per expert (decode). Each wave owns 16
-// output columns of one expert over the whole K: its lanes load the weight
-// rows straight from HBM into MFMA B-operand registers (32 contiguous bytes per
-// lane per 128-byte stage, so a wave reads full 128-byte lines of 16 rows), with
-// a kRing-deep register prefetch ring; the few A rows come from L2. Up to 16*R
-// rows of an expert are held at once; more rows loop (re-streaming the
-// weights), which only happens when the host's per-expert estimate is low.
-// Grid: (ceil(N_pad / 64), E_loc); experts without rows exit at once.
-// ---------------------------------------------------------------------------
-constexpr int kRing = 4;
-
-template <int DT, bool GATEUP, int R>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(const TileArgs p, int n_cols) {
-  const int e = blockIdx.y;
-  const GroupView gv = group_view(p, e);
-  const int row_beg = gv.row_beg, row_end = gv.row_end;
-  if (row_beg >= row_end) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const int n0 = (blockIdx.x * 4 + wave) * 16;
-  if (n0 >= n_cols) return;
-  const int64_t wcol = g4 * 32;
-  const uint8_t* wg = gv.w0 + (int64_t)(n0 + r16) * p.ldw_b + wcol;
-  const uint8_t* wu = GATEUP ? gv.w1 + (int64_t)(n0 + r16) * p.ldw_b + wcol : nullptr;
-  const int nblk = n0 >> 7;
-  const float* sw0 = DT == DMOE_FP8_E4M3 ? gv.s0 + (int64_t)nblk * p.nKb : nullptr;
-  const float* sw1 = (DT == DMOE_FP8_E4M3 && GATEUP) ? gv.s1 + (int64_t)nblk * p.nKb : nullptr;
-  constexpr int NM = GATEUP ? 2 : 1;  // weight matrices per wave
-
-  for (int m0 = row_beg; m0 < row_end; m0 += 16 * R) {
-    const uint8_t* arow[R];
-    bool aok[R];
-    int64_t srow[R][4];  // source rows of the 4 output rows this lane holds, for the A scales
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int m = m0 + 16 * i + r16;
-      aok[i] = m < row_end;
-      const int64_t src = aok[i] ? a_row(p, gv, m) : 0;
-      arow[i] = p.a + src * p.lda_b + wcol;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int mq = m0 + 16 * i + 4 * g4 + q;
-        srow[i][q] = mq < row_end ? a_row(p, gv, mq) : -1;
-      }
-    }
-    f32x4 acc[NM][R];
-#pragma unroll
-    for (int t = 0; t < NM; ++t)
-#pragma unroll
-      for (int i = 0; i < R; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    i32x4 rb[kRing][NM][2];
-    i32x4 ra[kRing][R][2];
-    auto issue = [&](int slot, int s) {
-      const int64_t off = (int64_t)s * kKB;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        rb[slot][0][h] = *reinterpret_cast<const i32x4*>(wg + off + 16 * h);
-        if (GATEUP) rb[slot][NM - 1][h] = *reinterpret_cast<const i32x4*>(wu + off + 16 * h);
-      }
-#pragma unroll
-      for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          ra[slot][i][h] = aok[i] ? *reinterpret_cast<const i32x4*>(arow[i] + off + 16 * h) : i32x4{0, 0, 0, 0};
-    };
-    auto compute = [&](int slot, int s) {
-      if constexpr (DT == DMOE_FP8_E4M3 && GATEUP) {
-        // exact products: E4M3 -> BF16 (exact), four BF16 MFMAs per 128-wide slice
-        const float w0s = sw0[s];
-        const float w1s = sw1[s];
-        i32x4 b16[NM][4];
-#pragma unroll
-        for (int t = 0; t < NM; ++t) {
-          e4m3x16_to_bf16(rb[slot][t][0], b16[t][0], b16[t][1]);
-          e4m3x16_to_bf16(rb[slot][t][1], b16[t][2], b16[t][3]);
-        }
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          i32x4 a16[4];
-          e4m3x16_to_bf16(ra[slot][i][0], a16[0], a16[1]);
-          e4m3x16_to_bf16(ra[slot][i][1], a16[2], a16[3]);
-          float sa[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) sa[q] = srow[i][q] >= 0 ? p.a_scales[srow[i][q] * p.ldas + s] : 0.f;
-#pragma unroll
-          for (int t = 0; t < NM; ++t) {
-            f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4)
-              part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a16[k4]),
-                                                             __builtin_bit_cast(bf16x8, b16[t][k4]), part, 0, 0, 0);
-            const float ws = t == 0 ? w0s : w1s;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[t][i][q] = fmaf(part[q], sa[q] * ws, acc[t][i][q]);
-          }
-        }
-      } else if constexpr (DT == DMOE_FP8_E4M3) {
-        const float w0s = sw0[s];
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const i32x8 fa = i32x8{ra[slot][i][0][0], ra[slot][i][0][1], ra[slot][i][0][2], ra[slot][i][0][3],
-                                 ra[slot][i][1][0], ra[slot][i][1][1], ra[slot][i][1][2], ra[slot][i][1][3]};
-          float sa[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) sa[q] = srow[i][q] >= 0 ? p.a_scales[srow[i][q] * p.ldas + s] : 0.f;
-          const i32x8 fb = i32x8{rb[slot][0][0][0], rb[slot][0][0][1], rb[slot][0][0][2], rb[slot][0][0][3],
-                                 rb[slot][0][1][0], rb[slot][0][1][1], rb[slot][0][1][2], rb[slot][0][1][3]};
-          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
-                                                                               0, 0, 0, 0, 0);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[0][i][q] = fmaf(part[q], sa[q] * w0s, acc[0][i][q]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const bf16x8 alo = __builtin_bit_cast(bf16x8, ra[slot][i][0]);
-          const bf16x8 ahi = __builtin_bit_cast(bf16x8, ra[slot][i][1]);
-#pragma unroll
-          for (int t = 0; t < NM; ++t) {
-            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, __builtin_bit_cast(bf16x8, rb[slot][t][0]),
-                                                                acc[t][i], 0, 0, 0);
-            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, __builtin_bit_cast(bf16x8, rb[slot][t][1]),
-                                                                acc[t][i], 0, 0, 0);
-          }
-        }
-      }
-    };
-
-#pragma unroll
-    for (int u = 0; u < kRing; ++u)
-      if (u < p.stages) issue(u, u);
-    for (int s0 = 0; s0 < p.stages; s0 += kRing) {
-#pragma unroll
-      for (int u = 0; u < kRing; ++u) {
-        const int s = s0 + u;
-        if (s < p.stages) {
-          compute(u, s);
-          if (s + kRing < p.stages) issue(u, s + kRing);
-        }
-      }
-    }
-
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + 16 * i + 4 * g4 + q;
-        if (m >= row_end) continue;
-        const float v = GATEUP ? silu(acc[0][i][q]) * acc[NM - 1][i][q] : acc[0][i][q];
-        p.out[(int64_t)m * p.ldo + n0 + r16] = (uint16_t)f32_to_bf16(v);
+        for (int j = 0; j < NT; ++j) orow[wcol0 + 16 * j + r16] = (uint16_t)f32_to_bf16(acc[i][j][r]);
       }
     }
   }
@@ -697,38 +505,23 @@ static hipError_t launch_gemm(const GemmArgs& g, bool gateup, hipStream_t stream
   p.xws1 = g.xws1;
   p.x_chunk = 0;
   // Few rows per expert on average: stream the weights (the tile schedule is not used).
-  // The extra group is cut into chunks of 16*R rows, one grid row each.
   if (use_stream) {
-    const int R = per_expert <= 16 ? 1 : 2;
-    p.x_chunk = 16 * R;
-    const int xchunks = (int)ceil_div(g.x_rows, p.x_chunk);
-    const dim3 sgrid((unsigned)(npad / 64), (unsigned)(g.E_loc + xchunks));
-    const int ncols = (int)npad;
-#define DMOE_STREAM(DTV, GU)                                                                         \
-  do {                                                                                               \
-    if (R == 1) gemm_stream_kernel<DTV, GU, 1><<<sgrid, 256, 0, stream>>>(p, ncols);                 \
-    else gemm_stream_kernel<DTV, GU, 2><<<sgrid, 256, 0, stream>>>(p, ncols);                        \
-  } while (0)
-    if (g.dtype == DMOE_FP8_E4M3) {
-      if (gateup) DMOE_STREAM(DMOE_FP8_E4M3, true);
-      else DMOE_STREAM(DMOE_FP8_E4M3, false);
-    } else {
-      if (gateup) DMOE_STREAM(DMOE_BF16, true);
-      else DMOE_STREAM(DMOE_BF16, false);
-    }
-#undef DMOE_STREAM
-    return hipGetLastError();
+    p.x_chunk = per_expert <= 16 ? 16 : 32;
+    return launch_gemm_stream(p, g.dtype, gateup, (int)per_expert, (int)npad, g.E_loc, stream);
   }
   // tile kernel: 128-byte stages for every mode (FP8: one 128-wide slice, BF16: 64 elements)
-  const int nNB = gateup ? (int)(npad / 64) : (int)(npad / 128);
-  const unsigned grid = (unsigned)((int64_t)cap * nNB);
   constexpr int NS = DMOE_TILE_NS;
+  constexpr int NT_GU = DMOE_TILE_NT_GATEUP, NT_DN = DMOE_TILE_NT_DOWN;
+  const int nt = gateup ? NT_GU : NT_DN;
+  const int nNB = gateup ? (int)(npad / (16 * nt)) : (int)ceil_div(npad, 32 * nt);
+  const unsigned grid = (unsigned)round_up((int64_t)cap * nNB, 8);
+  const int nv = (int)npad;
   if (g.dtype == DMOE_FP8_E4M3) {
-    if (gateup) gemm_tile_kernel<kModeFP8X, true, NS><<<grid, 256, 0, stream>>>(p, nNB);
-    else gemm_tile_kernel<kModeFP8, false, NS><<<grid, 256, 0, stream>>>(p, nNB);
+    if (gateup) gemm_tile_kernel<kModeFP8X, true, NS, NT_GU><<<grid, 256, 0, stream>>>(p, nNB, nv);
+    else gemm_tile_kernel<kModeFP8, false, NS, NT_DN><<<grid, 256, 0, stream>>>(p, nNB, nv);
   } else {
-    if (gateup) gemm_tile_kernel<kModeBF16, true, NS><<<grid, 256, 0, stream>>>(p, nNB);
-    else gemm_tile_kernel<kModeBF16, false, NS><<<grid, 256, 0, stream>>>(p, nNB);
+    if (gateup) gemm_tile_kernel<kModeBF16, true, NS, NT_GU><<<grid, 256, 0, stream>>>(p, nNB, nv);
+    else gemm_tile_kernel<kModeBF16, false, NS, NT_DN><<<grid, 256, 0, stream>>>(p, nNB, nv);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,98 @@
+// Shared pieces of the grouped expert GEMM kernels (gemm.hip: tile kernel for
+// many rows per expert; gemm_stream.hip: weight-streaming kernel for few).
+#pragma once
+
+#include "dmoe_internal.h"
+
+namespace dmoe {
+
+constexpr int kBM = 128;            // rows per tile
+constexpr int kKB = 128;            // K bytes per stage
+constexpr int kMaxSlices = 128;     // FP8 tile kernel: at most 128 scale slices along K (K <= 16384)
+
+struct TileArgs {
+  const uint8_t* a;
+  int64_t lda_b;  // bytes
+  const float* a_scales;
+  int64_t ldas;
+  const int32_t* row_token;
+  const int32_t* offsets;
+  const int2* tiles;
+  const int32_t* ntiles;
+  const uint8_t* w0;
+  const uint8_t* w1;
+  int64_t ldw_b;           // bytes
+  int64_t w_expert_b;      // bytes between experts
+  const float* ws0;
+  const float* ws1;
+  int nNb, nKb;            // 128-blocks along N (weight rows) and K
+  int stages;              // K stages of kKB bytes
+  uint16_t* out;
+  int64_t ldo;
+  int E_loc;
+  int x_rows, x_row0, x_a_base;  // extra (shared-expert) group, see GemmArgs
+  int x_chunk;                   // > 0: group indices >= E_loc are consecutive chunks of x_chunk rows
+  const uint8_t* xw0;
+  const uint8_t* xw1;
+  const float* xws0;
+  const float* xws1;
+};
+
+// Weights, scales and rows of group g: a routed expert (g < E_loc) or the extra group.
+struct GroupView {
+  const uint8_t* w0;
+  const uint8_t* w1;
+  const float* s0;  // block scales of this group, [nNb][nKb]
+  const float* s1;
+  int row_beg, row_end;
+  bool gather;  // A row = row_token[r]; otherwise A row = r - a_base
+  int a_base;
+};
+
+__device__ __forceinline__ GroupView group_view(const TileArgs& p, int g) {
+  GroupView v;
+  if (g < p.E_loc) {
+    v.w0 = p.w0 + g * p.w_expert_b;
+    v.w1 = p.w1 ? p.w1 + g * p.w_expert_b : nullptr;
+    v.s0 = p.ws0 ? p.ws0 + (int64_t)g * p.nNb * p.nKb : nullptr;
+    v.s1 = p.ws1 ? p.ws1 + (int64_t)g * p.nNb * p.nKb : nullptr;
+    v.row_beg = p.offsets[g];
+    v.row_end = p.offsets[g + 1];
+    v.gather = p.row_token != nullptr;
+    v.a_base = 0;
+  } else {
+    v.w0 = p.xw0;
+    v.w1 = p.xw1;
+    v.s0 = p.xws0;
+    v.s1 = p.xws1;
+    v.row_beg = p.x_row0 + (p.x_chunk > 0 ? (g - p.E_loc) * p.x_chunk : 0);
+    v.row_end = p.x_chunk > 0 ? min(p.x_row0 + p.x_rows, v.row_beg + p.x_chunk) : p.x_row0 + p.x_rows;
+    v.gather = false;
+    v.a_base = p.x_a_base;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int64_t a_row(const TileArgs& p, const GroupView& v, int r) {
+  return v.gather ? (int64_t)p.row_token[r] : (int64_t)(r - v.a_base);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
+
+__device__ __forceinline__ void e4m3x16_to_bf16(const i32x4 src, i32x4& lo, i32x4& hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  int out[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t v = (uint32_t)src[w];
+    out[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false));
+    out[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true));
+  }
+  lo = i32x4{out[0], out[1], out[2], out[3]};
+  hi = i32x4{out[4], out[5], out[6], out[7]};
+}
+
+hipError_t launch_gemm_stream(const TileArgs& p, int dtype, bool gateup, int rows_per_expert, int n_pad,
+                              int E_loc, hipStream_t stream);
+
+}  // namespace dmoe
