@@ -42,7 +42,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict
   }
   i32x4 out;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = (int)(f32_to_bf16(acc[2 * i]) | (f32_to_bf16(acc[2 * i + 1]) << 16));
+  for (int i = 0; i < 4; ++i) out[i] = (int)pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
   *reinterpret_cast<i32x4*>(y + t * ldy + c) = out;
 }
 

@@ -19,12 +19,19 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Round a float to bfloat16, nearest with ties to even (NaN stays a quiet NaN).
+// Round a float to bfloat16, nearest with ties to even, with v_cvt_pk_bf16_f32
+// (identical to the integer RNE rule on every non-NaN binary32 pattern,
+// denormals included; NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two floats to a packed BF16 pair (lo in bits 0-15), one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // ---------------------------------------------------------------------------

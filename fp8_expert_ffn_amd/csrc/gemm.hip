@@ -283,7 +283,8 @@ __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gem
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // weight rows (within the weight region) of this lane's subtiles
+  // weight rows (within the weight region) of this lane's subtiles; the
+  // weight fragment is the first MFMA operand, the A fragment the second
   auto brow = [&](int j) -> int {
     if (GATEUP) return (j < NH ? 0 : 16 * NT) + wn * 16 * NH + 16 * (j % NH) + r16;
     return wn * 16 * NT + 16 * j + r16;
@@ -299,20 +300,18 @@ __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gem
       fa[i][0] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4));
       fa[i][1] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4 + 1));
     }
-    // a_scale * w_scale of this stage's slice for each of the lane's rows
-    // (index 0: gate or down weights, 1: up weights)
-    float saw[GATEUP ? 2 : 1][MT][4];
+    // a_scale * w_scale of this stage's slice for the lane's row of each
+    // subtile (index 0: gate or down weights, 1: up weights)
+    float saw[GATEUP ? 2 : 1][MT];
     if constexpr (kScaled) {
       const float w0s = GATEUP ? lsw[0][s] : lsw[wn][s];
       const float w1s = GATEUP ? lsw[1][s] : 0.f;
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = lsa[64 * wm + 16 * i + 4 * g4 + r];
-          saw[0][i][r] = a * w0s;
-          if constexpr (GATEUP) saw[GATEUP ? 1 : 0][i][r] = a * w1s;
-        }
+      for (int i = 0; i < MT; ++i) {
+        const float a = lsa[64 * wm + 16 * i + r16];
+        saw[0][i] = a * w0s;
+        if constexpr (GATEUP) saw[GATEUP ? 1 : 0][i] = a * w1s;
+      }
     }
     if constexpr (MODE == kModeFP8X) {
       // exact products: codes -> BF16, four 16x16x32 MFMAs per 128-wide slice
@@ -337,10 +336,10 @@ __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gem
           f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int k4 = 0; k4 < 4; ++k4)
-            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a16[i][k4]),
-                                                           __builtin_bit_cast(bf16x8, b16[k4]), part, 0, 0, 0);
+            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b16[k4]),
+                                                           __builtin_bit_cast(bf16x8, a16[i][k4]), part, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[r], saw[wsel][i][r], acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[r], saw[wsel][i], acc[i][j][r]);
         }
       }
     } else if constexpr (MODE == kModeFP8) {
@@ -356,10 +355,10 @@ __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gem
         for (int i = 0; i < MT; ++i) {
           const i32x8 a8 = i32x8{fa[i][0][0], fa[i][0][1], fa[i][0][2], fa[i][0][3],
                                  fa[i][1][0], fa[i][1][1], fa[i][1][2], fa[i][1][3]};
-          const f32x4 pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+          const f32x4 pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
                                                                              0, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pr[r], saw[wsel][i][r], acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pr[r], saw[wsel][i], acc[i][j][r]);
         }
       }
     } else {
@@ -371,10 +370,10 @@ __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gem
         const i32x4 b1 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1));
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[i][0]),
-                                                              __builtin_bit_cast(bf16x8, b0), acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[i][1]),
-                                                              __builtin_bit_cast(bf16x8, b1), acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b0),
+                                                              __builtin_bit_cast(bf16x8, fa[i][0]), acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b1),
+                                                              __builtin_bit_cast(bf16x8, fa[i][1]), acc[i][j], 0, 0, 0);
         }
       }
     }
@@ -409,23 +408,28 @@ __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gem
   }
 
   if (!active) return;
-  // ---- epilogue: lane holds rows 4*g4 + r, column r16 of each 16x16 tile ----
+  // ---- epilogue: the weight fragment is the MFMA's first operand, so lane
+  // (r16, g4) holds row 16 i + r16 and the 4 consecutive columns 16 j + 4 g4 + r
+  // of each 16x16 tile: one 8-byte store per tile when the output allows it.
+  const bool wide = (p.ldo & 3) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 7) == 0;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
+    const int m = m0 + 64 * wm + 16 * i + r16;
+    if (m >= m_end) continue;
+    uint16_t* orow = p.out + (int64_t)m * p.ldo + wcol0 + 4 * g4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 64 * wm + 16 * i + 4 * g4 + r;
-      if (m >= m_end) continue;
-      uint16_t* orow = p.out + (int64_t)m * p.ldo;
-      if (GATEUP) {
+    for (int j = 0; j < (GATEUP ? NH : NT); ++j) {
+      float v[4];
 #pragma unroll
-        for (int j = 0; j < NH; ++j) {
-          const float h = silu(acc[i][j][r]) * acc[i][j + NH][r];
-          orow[wcol0 + 16 * j + r16] = (uint16_t)f32_to_bf16(h);
-        }
+      for (int r = 0; r < 4; ++r) v[r] = GATEUP ? silu(acc[i][j][r]) * acc[i][j + NH][r] : acc[i][j][r];
+      const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+      if (wide) {
+        *reinterpret_cast<uint2*>(orow + 16 * j) = make_uint2(lo, hi);
       } else {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) orow[wcol0 + 16 * j + r16] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+        orow[16 * j] = (uint16_t)lo;
+        orow[16 * j + 1] = (uint16_t)(lo >> 16);
+        orow[16 * j + 2] = (uint16_t)hi;
+        orow[16 * j + 3] = (uint16_t)(hi >> 16);
       }
     }
   }

@@ -39,20 +39,18 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const TileArgs p, int 
   constexpr int NM = GATEUP ? 2 : 1;  // weight matrices per wave
 
   for (int m0 = row_beg; m0 < row_end; m0 += 16 * R) {
+    // The weight fragment is the MFMA's first operand: lane (r16, g4) ends up
+    // with output row m0 + 16 i + r16 and columns n0 + 4 g4 .. n0 + 4 g4 + 3.
     const uint8_t* arow[R];
     bool aok[R];
-    int64_t srow[R][4];  // source rows of the 4 output rows this lane holds, for the A scales
+    const float* asc[R];  // this lane's row of A scales
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int m = m0 + 16 * i + r16;
       aok[i] = m < row_end;
       const int64_t src = aok[i] ? a_row(p, gv, m) : 0;
       arow[i] = p.a + src * p.lda_b + wcol;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int mq = m0 + 16 * i + 4 * g4 + q;
-        srow[i][q] = mq < row_end ? a_row(p, gv, mq) : -1;
-      }
+      asc[i] = DT == DMOE_FP8_E4M3 ? p.a_scales + src * p.ldas : nullptr;
     }
     f32x4 acc[NM][R];
 #pragma unroll
@@ -91,19 +89,17 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const TileArgs p, int 
           i32x4 a16[4];
           e4m3x16_to_bf16(ra[slot][i][0], a16[0], a16[1]);
           e4m3x16_to_bf16(ra[slot][i][1], a16[2], a16[3]);
-          float sa[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) sa[q] = srow[i][q] >= 0 ? p.a_scales[srow[i][q] * p.ldas + s] : 0.f;
+          const float sa = aok[i] ? asc[i][s] : 0.f;
 #pragma unroll
           for (int t = 0; t < NM; ++t) {
             f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k4 = 0; k4 < 4; ++k4)
-              part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a16[k4]),
-                                                             __builtin_bit_cast(bf16x8, b16[t][k4]), part, 0, 0, 0);
-            const float ws = t == 0 ? w0s : w1s;
+              part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b16[t][k4]),
+                                                             __builtin_bit_cast(bf16x8, a16[k4]), part, 0, 0, 0);
+            const float saw = sa * (t == 0 ? w0s : w1s);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[t][i][q] = fmaf(part[q], sa[q] * ws, acc[t][i][q]);
+            for (int q = 0; q < 4; ++q) acc[t][i][q] = fmaf(part[q], saw, acc[t][i][q]);
           }
         }
       } else if constexpr (DT == DMOE_FP8_E4M3) {
@@ -112,15 +108,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const TileArgs p, int 
         for (int i = 0; i < R; ++i) {
           const i32x8 fa = i32x8{ra[slot][i][0][0], ra[slot][i][0][1], ra[slot][i][0][2], ra[slot][i][0][3],
                                  ra[slot][i][1][0], ra[slot][i][1][1], ra[slot][i][1][2], ra[slot][i][1][3]};
-          float sa[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) sa[q] = srow[i][q] >= 0 ? p.a_scales[srow[i][q] * p.ldas + s] : 0.f;
+          const float saw = (aok[i] ? asc[i][s] : 0.f) * w0s;
           const i32x8 fb = i32x8{rb[slot][0][0][0], rb[slot][0][0][1], rb[slot][0][0][2], rb[slot][0][0][3],
                                  rb[slot][0][1][0], rb[slot][0][1][1], rb[slot][0][1][2], rb[slot][0][1][3]};
-          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
+          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
                                                                                0, 0, 0, 0, 0);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[0][i][q] = fmaf(part[q], sa[q] * w0s, acc[0][i][q]);
+          for (int q = 0; q < 4; ++q) acc[0][i][q] = fmaf(part[q], saw, acc[0][i][q]);
         }
       } else {
 #pragma unroll
@@ -129,9 +123,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const TileArgs p, int 
           const bf16x8 ahi = __builtin_bit_cast(bf16x8, ra[slot][i][1]);
 #pragma unroll
           for (int t = 0; t < NM; ++t) {
-            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, __builtin_bit_cast(bf16x8, rb[slot][t][0]),
+            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rb[slot][t][0]), alo,
                                                                 acc[t][i], 0, 0, 0);
-            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, __builtin_bit_cast(bf16x8, rb[slot][t][1]),
+            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rb[slot][t][1]), ahi,
                                                                 acc[t][i], 0, 0, 0);
           }
         }
@@ -152,14 +146,22 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const TileArgs p, int 
       }
     }
 
+    const bool wide = (p.ldo & 3) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 7) == 0;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
+      if (!aok[i]) continue;
+      float v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + 16 * i + 4 * g4 + q;
-        if (m >= row_end) continue;
-        const float v = GATEUP ? silu(acc[0][i][q]) * acc[NM - 1][i][q] : acc[0][i][q];
-        p.out[(int64_t)m * p.ldo + n0 + r16] = (uint16_t)f32_to_bf16(v);
+      for (int q = 0; q < 4; ++q) v[q] = GATEUP ? silu(acc[0][i][q]) * acc[NM - 1][i][q] : acc[0][i][q];
+      const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+      uint16_t* o = p.out + (int64_t)(m0 + 16 * i + r16) * p.ldo + n0 + 4 * g4;
+      if (wide) {
+        *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+      } else {
+        o[0] = (uint16_t)lo;
+        o[1] = (uint16_t)(lo >> 16);
+        o[2] = (uint16_t)hi;
+        o[3] = (uint16_t)(hi >> 16);
       }
     }
   }
