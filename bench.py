@@ -49,8 +49,8 @@ def build_layer(cfg, dev):
 
 
 def uses_stream_kernel(cfg) -> bool:
-    """The library's choice for the grouped GEMMs: weight streaming when the host bound on rows per local
-    expert, ceil(T*K / E_loc), is at most 32; tile GEMM otherwise."""
+    """The library's choice for the grouped GEMMs: the weight-streaming kernel when the host bound on rows per
+    local expert, ceil(T*K / E_loc), is at most 32; tile GEMM otherwise."""
     return -(-cfg.T * cfg.K // cfg.E_loc) <= 32
 
 
@@ -244,7 +244,7 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TFLOPS[cfg.dtype], 4), "traffic": None}
     stream_k = uses_stream_kernel(cfg)
-    kname = f"{'gemm_stream_kernel' if stream_k else 'gemm_tile_kernel'}<{cfg.dtype}, gate/up>"
+    kname = f"{'gemm_stage_kernel' if stream_k else 'gemm_tile_kernel'}<{cfg.dtype}, gate/up>"
     roof["kernel"] = kname + (" (routed experts + shared expert as an extra group)" if shared_fused(cfg)
                               else " (routed experts)")
     rec = traffic_record(cfg.name, kname, kernel_source_hash(stream_k))

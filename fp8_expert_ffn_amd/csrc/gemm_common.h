@@ -2,6 +2,8 @@
 // many rows per expert; gemm_stream.hip: weight-streaming kernel for few).
 #pragma once
 
+#include <type_traits>
+
 #include "dmoe_internal.h"
 
 namespace dmoe {
@@ -90,6 +92,50 @@ __device__ __forceinline__ void e4m3x16_to_bf16(const i32x4 src, i32x4& lo, i32x
   }
   lo = i32x4{out[0], out[1], out[2], out[3]};
   hi = i32x4{out[4], out[5], out[6], out[7]};
+}
+
+// LDS rows are 128 bytes; their 16-byte units are XOR-swizzled by (row >> 1) & 7.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Asynchronous global -> LDS copies of 16 (or 4) bytes per lane: lane l writes
+// LDS bytes [base + 16 l, +16) (resp. [base + 4 l, +4)); base is wave-uniform
+// and goes through M0. Issued from asm so that the compiler's wait insertion,
+// which cannot tell the pipeline's LDS buffers apart, does not make every LDS
+// read wait for every copy in flight; the pipeline waits on vmcnt itself. The
+// instruction writes no register, so nothing of it is live after issue.
+__device__ __forceinline__ void lds_copy16(const void* gptr, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const void* gptr, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(m0) : "memory", "m0");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose release
+// half would wait for every outstanding global load, including the younger
+// pipeline stages). Callers order memory with explicit s_waitcnt first; the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 hipError_t launch_gemm_stream(const TileArgs& p, int dtype, bool gateup, int rows_per_expert, int n_pad,

@@ -1,4 +1,5 @@
-// Grouped expert GEMMs for few rows per expert (decode): weight streaming.
+// Grouped expert GEMMs for few rows per expert (decode): weight streaming
+// through LDS.
 //
 // Same operation as the tile kernel in gemm.hip (gate/up with fused SwiGLU, or
 // down; FP8 block-scale promotion per 128-wide K slice; Transformers docs
@@ -9,87 +10,117 @@
 namespace dmoe {
 
 // ---------------------------------------------------------------------------
-// Weight-streaming kernel for few rows per expert (decode). Each wave owns 16
-// output columns of one expert over the whole K: its lanes load the weight
-// rows straight from HBM into MFMA B-operand registers (32 contiguous bytes per
-// lane per 128-byte stage, so a wave reads full 128-byte lines of 16 rows), with
-// a kRing-deep register prefetch ring; the few A rows come from L2. Up to 16*R
-// rows of an expert are held at once; more rows loop (re-streaming the
-// weights), which only happens when the host's per-expert estimate is low.
-// Grid: (ceil(N_pad / 64), E_loc); experts without rows exit at once.
+// Weight-streaming kernel for few rows per expert (decode). A workgroup
+// owns 64 output columns of one group: WR = 128 weight rows for gate/up (64
+// gate + 64 up) or 64 for down. Every 128-byte K stage of those rows, of the
+// group's (up to 16 R) A rows and of their FP8 scales moves global -> LDS with
+// direct loads (each instruction covers 8 whole 128-byte lines) through a
+// kStageRing-deep ring; wave w then multiplies the 16 columns 16 w .. 16 w + 15
+// from LDS fragments. Grid: (ceil(N_pad / 64), E_loc + chunks).
 // ---------------------------------------------------------------------------
-constexpr int kRing = 4;
+#ifndef DMOE_STAGE_RING
+#define DMOE_STAGE_RING 4
+#endif
+constexpr int kStageRing = DMOE_STAGE_RING;
 
 template <int DT, bool GATEUP, int R>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(const TileArgs p, int n_cols) {
-  const int e = blockIdx.y;
-  const GroupView gv = group_view(p, e);
+__global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n_cols) {
+  constexpr bool kFP8 = DT == DMOE_FP8_E4M3;
+  constexpr int WR = GATEUP ? 128 : 64;   // weight rows per workgroup
+  constexpr int AR = 16 * R;              // A rows per pass
+  constexpr int kRows = WR + AR;
+  constexpr int NS = kStageRing;
+  constexpr int kCopies = WR / 32 + 1 + (kFP8 ? 1 : 0);  // direct copies per wave per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][kRows * 128];
+  __shared__ __attribute__((aligned(256))) float lsa[NS][32];
+  __shared__ float lsw[2][kMaxSlices];
+  asm volatile("" ::"v"(&ring[0][0]), "v"(&lsa[0][0]) : "memory");
+
+  const GroupView gv = group_view(p, blockIdx.y);
   const int row_beg = gv.row_beg, row_end = gv.row_end;
   if (row_beg >= row_end) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const int n0 = (blockIdx.x * 4 + wave) * 16;
+  const int n0 = blockIdx.x * 64;
   if (n0 >= n_cols) return;
-  const int64_t wcol = g4 * 32;
-  const uint8_t* wg = gv.w0 + (int64_t)(n0 + r16) * p.ldw_b + wcol;
-  const uint8_t* wu = GATEUP ? gv.w1 + (int64_t)(n0 + r16) * p.ldw_b + wcol : nullptr;
-  const int nblk = n0 >> 7;
-  const float* sw0 = DT == DMOE_FP8_E4M3 ? gv.s0 + (int64_t)nblk * p.nKb : nullptr;
-  const float* sw1 = (DT == DMOE_FP8_E4M3 && GATEUP) ? gv.s1 + (int64_t)nblk * p.nKb : nullptr;
-  constexpr int NM = GATEUP ? 2 : 1;  // weight matrices per wave
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int S = p.stages;
 
-  for (int m0 = row_beg; m0 < row_end; m0 += 16 * R) {
-    // The weight fragment is the MFMA's first operand: lane (r16, g4) ends up
-    // with output row m0 + 16 i + r16 and columns n0 + 4 g4 .. n0 + 4 g4 + 3.
-    const uint8_t* arow[R];
-    bool aok[R];
-    const float* asc[R];  // this lane's row of A scales
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int m = m0 + 16 * i + r16;
-      aok[i] = m < row_end;
-      const int64_t src = aok[i] ? a_row(p, gv, m) : 0;
-      arow[i] = p.a + src * p.lda_b + wcol;
-      asc[i] = DT == DMOE_FP8_E4M3 ? p.a_scales + src * p.ldas : nullptr;
+  // weight block scales of the workgroup's 64 columns (one 128-row block)
+  if constexpr (kFP8) {
+    for (int i = tid; i < (GATEUP ? 2 : 1) * p.nKb; i += 256) {
+      const int w = i / p.nKb, sl = i - w * p.nKb;
+      lsw[w][sl] = (w == 0 ? gv.s0 : gv.s1)[(int64_t)(n0 >> 7) * p.nKb + sl];
     }
+  }
+  __syncthreads();
+
+  // weight copies: copy i of wave w fills LDS rows 8 (4 i + w) .. + 7
+  const uint8_t* srcB[WR / 32];
+#pragma unroll
+  for (int i = 0; i < WR / 32; ++i) {
+    const int row = 8 * (4 * i + wave) + (lane >> 3);
+    const uint8_t* base = (GATEUP && row >= 64) ? gv.w1 : gv.w0;
+    srcB[i] = base + (int64_t)(n0 + (row & 63)) * p.ldw_b + 16 * swz(row, lane & 7);
+  }
+
+  for (int m0 = row_beg; m0 < row_end; m0 += AR) {
+    // A copy of wave w: rows (AR / 4) w .. + AR / 4 - 1 (R = 1: lanes 0..31)
+    const int arow_l = (AR / 4) * wave + (lane >> 3);
+    const bool a_lane = lane < 2 * AR;  // 8 lanes per row, AR / 4 rows per wave
+    const int am = m0 + arow_l;
+    const int64_t a_src = a_row(p, gv, am < row_end ? am : m0);
+    const uint8_t* srcA = p.a + a_src * p.lda_b + 16 * swz(WR + arow_l, lane & 7);
+    // scale copy of wave w: rows 8 w + lane (lanes 0..7)
+    const int srow_l = 8 * wave + lane;
+    const int sm = m0 + srow_l;
+    const float* srcS = kFP8 ? p.a_scales + a_row(p, gv, (lane < 8 && sm < row_end) ? sm : m0) * p.ldas : nullptr;
+
+    auto issue = [&](int s) {
+      uint8_t* st = ring[s % NS];
+      const int64_t off = (int64_t)s * 128;
+#pragma unroll
+      for (int i = 0; i < WR / 32; ++i) lds_copy16(srcB[i] + off, st + (8 * (4 * i + wave)) * 128);
+      if (a_lane) lds_copy16(srcA + off, st + (WR + (AR / 4) * wave) * 128);
+      if (kFP8 && lane < 8) lds_copy4(srcS + s, &lsa[s % NS][8 * wave]);
+    };
+
+    constexpr int NM = GATEUP ? 2 : 1;
     f32x4 acc[NM][R];
 #pragma unroll
     for (int t = 0; t < NM; ++t)
 #pragma unroll
       for (int i = 0; i < R; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    i32x4 rb[kRing][NM][2];
-    i32x4 ra[kRing][R][2];
-    auto issue = [&](int slot, int s) {
-      const int64_t off = (int64_t)s * kKB;
+    auto compute = [&](int s) {
+      const uint8_t* st = ring[s % NS];
+      // weight fragments of this wave's 16 columns (first MFMA operand), A fragments (second)
+      i32x4 fb[NM][2], fa[R][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        rb[slot][0][h] = *reinterpret_cast<const i32x4*>(wg + off + 16 * h);
-        if (GATEUP) rb[slot][NM - 1][h] = *reinterpret_cast<const i32x4*>(wu + off + 16 * h);
+      for (int t = 0; t < NM; ++t) {
+        const int row = 64 * t + 16 * wave + r16;
+        fb[t][0] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4));
+        fb[t][1] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4 + 1));
       }
 #pragma unroll
-      for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          ra[slot][i][h] = aok[i] ? *reinterpret_cast<const i32x4*>(arow[i] + off + 16 * h) : i32x4{0, 0, 0, 0};
-    };
-    auto compute = [&](int slot, int s) {
-      if constexpr (DT == DMOE_FP8_E4M3 && GATEUP) {
+      for (int i = 0; i < R; ++i) {
+        const int row = WR + 16 * i + r16;
+        fa[i][0] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4));
+        fa[i][1] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4 + 1));
+      }
+      if constexpr (kFP8 && GATEUP) {
         // exact products: E4M3 -> BF16 (exact), four BF16 MFMAs per 128-wide slice
-        const float w0s = sw0[s];
-        const float w1s = sw1[s];
         i32x4 b16[NM][4];
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
-          e4m3x16_to_bf16(rb[slot][t][0], b16[t][0], b16[t][1]);
-          e4m3x16_to_bf16(rb[slot][t][1], b16[t][2], b16[t][3]);
+          e4m3x16_to_bf16(fb[t][0], b16[t][0], b16[t][1]);
+          e4m3x16_to_bf16(fb[t][1], b16[t][2], b16[t][3]);
         }
 #pragma unroll
         for (int i = 0; i < R; ++i) {
           i32x4 a16[4];
-          e4m3x16_to_bf16(ra[slot][i][0], a16[0], a16[1]);
-          e4m3x16_to_bf16(ra[slot][i][1], a16[2], a16[3]);
-          const float sa = aok[i] ? asc[i][s] : 0.f;
+          e4m3x16_to_bf16(fa[i][0], a16[0], a16[1]);
+          e4m3x16_to_bf16(fa[i][1], a16[2], a16[3]);
+          const float sa = lsa[s % NS][16 * i + r16];
 #pragma unroll
           for (int t = 0; t < NM; ++t) {
             f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -97,64 +128,63 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const TileArgs p, int 
             for (int k4 = 0; k4 < 4; ++k4)
               part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b16[t][k4]),
                                                              __builtin_bit_cast(bf16x8, a16[k4]), part, 0, 0, 0);
-            const float saw = sa * (t == 0 ? w0s : w1s);
+            const float saw = sa * lsw[t][s];
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[t][i][q] = fmaf(part[q], saw, acc[t][i][q]);
           }
         }
-      } else if constexpr (DT == DMOE_FP8_E4M3) {
-        const float w0s = sw0[s];
+      } else if constexpr (kFP8) {
+        const i32x8 b8 = i32x8{fb[0][0][0], fb[0][0][1], fb[0][0][2], fb[0][0][3],
+                               fb[0][1][0], fb[0][1][1], fb[0][1][2], fb[0][1][3]};
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          const i32x8 fa = i32x8{ra[slot][i][0][0], ra[slot][i][0][1], ra[slot][i][0][2], ra[slot][i][0][3],
-                                 ra[slot][i][1][0], ra[slot][i][1][1], ra[slot][i][1][2], ra[slot][i][1][3]};
-          const float saw = (aok[i] ? asc[i][s] : 0.f) * w0s;
-          const i32x8 fb = i32x8{rb[slot][0][0][0], rb[slot][0][0][1], rb[slot][0][0][2], rb[slot][0][0][3],
-                                 rb[slot][0][1][0], rb[slot][0][1][1], rb[slot][0][1][2], rb[slot][0][1][3]};
-          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
+          const i32x8 a8 = i32x8{fa[i][0][0], fa[i][0][1], fa[i][0][2], fa[i][0][3],
+                                 fa[i][1][0], fa[i][1][1], fa[i][1][2], fa[i][1][3]};
+          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
                                                                                0, 0, 0, 0, 0);
+          const float saw = lsa[s % NS][16 * i + r16] * lsw[0][s];
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[0][i][q] = fmaf(part[q], saw, acc[0][i][q]);
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const bf16x8 alo = __builtin_bit_cast(bf16x8, ra[slot][i][0]);
-          const bf16x8 ahi = __builtin_bit_cast(bf16x8, ra[slot][i][1]);
+        for (int i = 0; i < R; ++i)
 #pragma unroll
           for (int t = 0; t < NM; ++t) {
-            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rb[slot][t][0]), alo,
-                                                                acc[t][i], 0, 0, 0);
-            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rb[slot][t][1]), ahi,
-                                                                acc[t][i], 0, 0, 0);
+            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[t][0]),
+                                                                __builtin_bit_cast(bf16x8, fa[i][0]), acc[t][i], 0, 0, 0);
+            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[t][1]),
+                                                                __builtin_bit_cast(bf16x8, fa[i][1]), acc[t][i], 0, 0, 0);
           }
-        }
       }
     };
 
-#pragma unroll
-    for (int u = 0; u < kRing; ++u)
-      if (u < p.stages) issue(u, u);
-    for (int s0 = 0; s0 < p.stages; s0 += kRing) {
-#pragma unroll
-      for (int u = 0; u < kRing; ++u) {
-        const int s = s0 + u;
-        if (s < p.stages) {
-          compute(u, s);
-          if (s + kRing < p.stages) issue(u, s + kRing);
-        }
+    // ---- NS-stage ring: stage s lives in buffer s % NS ----
+    for (int s = 0; s < NS - 1 && s < S; ++s) issue(s);
+    for (int s = 0; s < S; ++s) {
+      if (s + NS - 1 < S) {
+        issue(s + NS - 1);
+        wait_vmcnt<kCopies * (NS - 1)>();  // stage s complete: at most the NS-1 younger stages in flight
+      } else {
+        wait_vmcnt<0>();
       }
+      stage_barrier();  // every wave's copies of stage s have landed in LDS
+      compute(s);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
+      stage_barrier();  // buffer s % NS may be refilled
     }
 
+    // ---- epilogue: lane (r16, g4) holds row m0 + 16 i + r16, columns n0 + 16 wave + 4 g4 + q ----
     const bool wide = (p.ldo & 3) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 7) == 0;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      if (!aok[i]) continue;
+      const int m = m0 + 16 * i + r16;
+      if (m >= row_end) continue;
       float v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[q] = GATEUP ? silu(acc[0][i][q]) * acc[NM - 1][i][q] : acc[0][i][q];
       const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-      uint16_t* o = p.out + (int64_t)(m0 + 16 * i + r16) * p.ldo + n0 + 4 * g4;
+      uint16_t* o = p.out + (int64_t)m * p.ldo + n0 + 16 * wave + 4 * g4;
       if (wide) {
         *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
       } else {
@@ -176,8 +206,8 @@ hipError_t launch_gemm_stream(const TileArgs& p, int dtype, bool gateup, int row
   const dim3 grid((unsigned)(n_pad / 64), (unsigned)(E_loc + xchunks));
 #define DMOE_STREAM(DTV, GU)                                                                         \
   do {                                                                                               \
-    if (R == 1) gemm_stream_kernel<DTV, GU, 1><<<grid, 256, 0, stream>>>(p, n_pad);                  \
-    else gemm_stream_kernel<DTV, GU, 2><<<grid, 256, 0, stream>>>(p, n_pad);                         \
+    if (R == 1) gemm_stage_kernel<DTV, GU, 1><<<grid, 256, 0, stream>>>(p, n_pad);                   \
+    else gemm_stage_kernel<DTV, GU, 2><<<grid, 256, 0, stream>>>(p, n_pad);                          \
   } while (0)
   if (dtype == DMOE_FP8_E4M3) {
     if (gateup) DMOE_STREAM(DMOE_FP8_E4M3, true);
