@@ -248,9 +248,10 @@ def dmoe_forward(desc: LayerDesc, ptrs: LayerPtrs, ws: torch.Tensor, stream=None
 
 
 def dmoe_forward_timed(desc: LayerDesc, ptrs: LayerPtrs, ws: torch.Tensor, events, stream=None) -> None:
-    """events: DMOE_STAGES + 1 torch.cuda.Event(enable_timing=True), already recorded once (created)."""
+    """events: DMOE_STAGES + 1 entries, each a torch.cuda.Event(enable_timing=True) already recorded once
+    (so that its HIP event exists) or None (that boundary is not recorded)."""
     if len(events) != DMOE_STAGES + 1:
         raise ValueError(f"need {DMOE_STAGES + 1} events")
-    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    arr = (ctypes.c_void_p * len(events))(*[(e.cuda_event if e is not None else None) for e in events])
     _check(lib().dmoe_forward_timed(ctypes.byref(desc), ctypes.byref(ptrs), ptr(ws), ws.numel(),
                                     stream_handle(stream), arr))

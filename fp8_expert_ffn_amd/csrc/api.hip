@@ -477,7 +477,10 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
   hipError_t e = hipSuccess;
   int stage = 0;
   // Marks the end of a stage (and the start of the next) when the caller asked for events.
-  auto mark = [&]() -> hipError_t { return ev ? hipEventRecord(ev[stage++], stream) : hipSuccess; };
+  auto mark = [&]() -> hipError_t {
+    const int i = stage++;
+    return (ev && ev[i]) ? hipEventRecord(ev[i], stream) : hipSuccess;
+  };
 #define STEP(call, what)                               \
   do {                                                 \
     e = (call);                                        \

@@ -257,8 +257,10 @@ dmoe_status dmoe_forward(const dmoe_layer_desc* desc, const dmoe_layer_ptrs* ptr
  * before stage i and event DMOE_STAGES after the last one. Stages, in order:
  * 0 router logits (empty when logits are given), 1 route, 2 permute and tile
  * schedule, 3 quantise x (FP8), 4 gate/up + SwiGLU, 5 quantise h (FP8),
- * 6 down, 7 shared expert, 8 combine. Recording events adds stream markers
- * only; the results are identical to dmoe_forward.
+ * 6 down, 7 shared expert, 8 combine. A NULL entry is skipped (each recorded
+ * event is a stream marker that costs a few microseconds of queue time).
+ * Recording events adds stream markers only; the results are identical to
+ * dmoe_forward.
  */
 #define DMOE_STAGES 9
 dmoe_status dmoe_forward_timed(const dmoe_layer_desc* desc, const dmoe_layer_ptrs* ptrs, void* ws, size_t ws_bytes,

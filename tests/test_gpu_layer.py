@@ -144,3 +144,30 @@ def test_separate_entry_points_match_forward():
     dm.dmoe_combine(o, tr, w, s, cfg.T_s, cfg.H, y)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), full.view(torch.int16))
+
+
+def test_timed_forward_matches_forward():
+    """dmoe_forward_timed with every stage boundary, with only the gate/up boundaries (NULL entries elsewhere),
+    and dmoe_forward produce bit-identical outputs; the recorded events bracket non-negative intervals."""
+    import fp8_expert_ffn_amd as dm
+    cfg, layer, x, x_bits, wr, given, ref = _run("prefill_small_fp8")
+    wdev = torch.from_numpy(wr).to(DEV)
+    d, p, ws, out = layer.make_call(x, cfg.T_s, w_router=wdev)
+    y = out["y"]
+    stream = torch.cuda.current_stream()
+    dm.dmoe_forward(d, p, ws)
+    torch.cuda.synchronize()
+    y0 = y.clone()
+    n = dm.DMOE_STAGES + 1
+    gu = dm.STAGE_NAMES.index("gateup")
+    for which in (set(range(n)), {gu, gu + 1}):
+        ev = [torch.cuda.Event(enable_timing=True) if s in which else None for s in range(n)]
+        for e in ev:
+            if e is not None:
+                e.record(stream)
+        torch.cuda.synchronize()
+        y.zero_()
+        dm.dmoe_forward_timed(d, p, ws, ev)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
+        assert ev[gu].elapsed_time(ev[gu + 1]) >= 0.0
