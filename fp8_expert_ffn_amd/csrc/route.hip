@@ -37,18 +37,19 @@ __device__ __forceinline__ void split3_bf16(const float (&w)[8], bf16x8& hi, bf1
   }
 }
 
-template <int TT, int EE>
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x, int64_t ldx,
-                                                            const float* __restrict__ w_r, int T, int H, int E,
-                                                            float* __restrict__ logits) {
-  __shared__ f32x4 red[3][TT * EE][kWave];
+// NW waves split H into NW equal ranges (H % (32 NW) == 0).
+template <int TT, int EE, int NW>
+__global__ __launch_bounds__(64 * NW) void router_logits_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                                const float* __restrict__ w_r, int T, int H, int E,
+                                                                float* __restrict__ logits) {
+  __shared__ f32x4 red[NW - 1][TT * EE][kWave];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * 16 * TT;
   const int e0 = blockIdx.y * 16 * EE;
   const int r16 = lane & 15;
   const int kg = (lane >> 4) * 8;
-  const int kq = H / 4;
+  const int kq = H / NW;
   const int kbeg = wave * kq;
 
   const uint16_t* xrow[TT];
@@ -59,13 +60,13 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     xok[i] = t < T;
     xrow[i] = x + (int64_t)(xok[i] ? t : 0) * ldx + kg;
   }
-  const float* wrow[EE];
+  int64_t wrow[EE];
   bool wok[EE];
 #pragma unroll
   for (int j = 0; j < EE; ++j) {
     const int e = e0 + 16 * j + r16;
     wok[j] = e < E;
-    wrow[j] = w_r + (int64_t)(wok[j] ? e : 0) * H + kg;
+    wrow[j] = (int64_t)(wok[j] ? e : 0) * H + kg;
   }
 
   f32x4 acc[TT][EE];
@@ -86,8 +87,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     for (int j = 0; j < EE; ++j) {
       float wv[8];
       if (wok[j]) {
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wrow[j] + k);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wrow[j] + k + 4);
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(w_r + wrow[j] + k);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(w_r + wrow[j] + k + 4);
         wv[0] = w0[0]; wv[1] = w0[1]; wv[2] = w0[2]; wv[3] = w0[3];
         wv[4] = w1[0]; wv[5] = w1[1]; wv[6] = w1[2]; wv[7] = w1[3];
       } else {
@@ -118,9 +119,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 #pragma unroll
     for (int j = 0; j < EE; ++j) {
       f32x4 s = acc[i][j];
-      s += red[0][i * EE + j][lane];
-      s += red[1][i * EE + j][lane];
-      s += red[2][i * EE + j][lane];
+#pragma unroll
+      for (int w = 0; w < NW - 1; ++w) s += red[w][i * EE + j][lane];  // fixed wave order: deterministic
       const int e = e0 + 16 * j + r16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -134,11 +134,15 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 hipError_t launch_router_logits(const uint16_t* x, int64_t ldx, const float* w_r, int T, int H, int E,
                                 float* logits, hipStream_t stream) {
   if (T <= 256) {
+    // few tokens: the weight read dominates; 16 waves per workgroup keep more of it in flight
     dim3 grid((T + 15) / 16, (E + 15) / 16);
-    router_logits_kernel<1, 1><<<grid, 256, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
+    if (H % 512 == 0)
+      router_logits_kernel<1, 1, 16><<<grid, 1024, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
+    else
+      router_logits_kernel<1, 1, 4><<<grid, 256, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
   } else {
     dim3 grid((T + 63) / 64, (E + 63) / 64);
-    router_logits_kernel<4, 4><<<grid, 256, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
+    router_logits_kernel<4, 4, 4><<<grid, 256, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
   }
   return hipGetLastError();
 }

@@ -144,6 +144,29 @@ def test_quant_act_exhaustive_bf16_patterns():
         _quant_case(block)
 
 
+def test_quant_act_scale_sweep_all_patterns():
+    """Scales across the whole exponent range (amax every 0x100 BF16 patterns, denormal to max finite), each with
+    every BF16 value inside its slice range: the scaled quotient and its E4M3 code are bit-exact everywhere."""
+    bits = np.arange(65536, dtype=np.uint32)
+    vals = (bits << np.uint32(16)).view(np.float32)
+    finite = bits[np.isfinite(vals)].astype(np.uint16)
+    fvals = (finite.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    blocks = []
+    for amax_bits in list(range(0x0001, 0x7F80, 0x100)) + [0x7F7F]:
+        amax = float((np.uint32(amax_bits) << np.uint32(16)).view(np.float32))
+        sel = finite[np.abs(fvals) <= amax]
+        n = -(-sel.size // 127)
+        block = np.zeros((n, 128), dtype=np.uint16)
+        flat = np.zeros(n * 127, dtype=np.uint16)
+        flat[:sel.size] = sel
+        block[:, 1:] = flat.reshape(n, 127)
+        block[:, 0] = amax_bits
+        blocks.append(block)
+    x = np.concatenate(blocks)
+    say(f"quant_act scale sweep: {len(blocks)} scales, {x.shape[0]} slices")
+    _quant_case(x)
+
+
 def test_quant_act_zero_and_sign_cases():
     x = np.zeros((3, 256), dtype=np.uint16)
     x[1, :] = 0x8000          # -0.0 everywhere: scale 0, all codes 0
