@@ -324,7 +324,7 @@ dmoe_status dmoe_combine(const uint16_t* o, int64_t ldo, const int32_t* token_ro
                          const uint16_t* s_out, int64_t lds, int32_t T_s, int32_t T, int32_t K, int32_t H,
                          uint16_t* y, int64_t ldy, hipStream_t stream) {
   REQ(T >= 0 && T_s >= 0, DMOE_ERR_INVALID_ARG, "negative token count");
-  REQ(K >= 1 && K <= 1024, DMOE_ERR_INVALID_ARG, "K = %d outside [1, 1024]", K);
+  REQ(K >= 1 && K <= 64, DMOE_ERR_INVALID_ARG, "K = %d outside [1, 64]", K);
   REQ(H > 0 && H % 8 == 0, DMOE_ERR_INVALID_ARG, "H = %d must be a positive multiple of 8", H);
   if (T == 0) return ok();
   REQ_PTR(o, "o");

@@ -7,51 +7,68 @@
 
 namespace dmoe {
 
-// Grid (T, ceil(H / 1024)): one workgroup per token and 1024-column chunk,
-// 8 BF16 columns (16 bytes) per thread.
-__global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ o, int64_t ldo,
-                                                      const int32_t* __restrict__ token_row,
-                                                      const float* __restrict__ w,
-                                                      const uint16_t* __restrict__ s, int64_t lds, int T_s, int K,
-                                                      int H, uint16_t* __restrict__ y, int64_t ldy) {
+// One workgroup per token; each thread owns 8 consecutive BF16 columns (16
+// bytes) and walks the row in steps of 8 * blockDim.x columns. The first wave
+// compacts the token's local slots (row, weight) into LDS in slot order, so the
+// row loads of all slots are independent of each other and of the slot table.
+__global__ __launch_bounds__(1024) void combine_kernel(const uint16_t* __restrict__ o, int64_t ldo,
+                                                       const int32_t* __restrict__ token_row,
+                                                       const float* __restrict__ w,
+                                                       const uint16_t* __restrict__ s, int64_t lds, int T_s, int K,
+                                                       int H, uint16_t* __restrict__ y, int64_t ldy) {
+  __shared__ int32_t srow[64];
+  __shared__ float sw[64];
+  __shared__ int nslot;
   const int64_t t = blockIdx.x;
-  const int c = blockIdx.y * 1024 + threadIdx.x * 8;
-  if (c >= H) return;
+  if (threadIdx.x < 64) {  // K <= 64
+    const int k = threadIdx.x;
+    const int32_t r = k < K ? token_row[t * K + k] : -1;
+    const uint64_t valid = __ballot(r >= 0);
+    const int pos = __popcll(valid & ((1ull << k) - 1ull));
+    if (r >= 0) {
+      srow[pos] = r;
+      sw[pos] = w[t * K + k];
+    }
+    if (k == 0) nslot = __popcll(valid);
+  }
+  __syncthreads();
+  const int n = nslot;
   const bool shared = s != nullptr && t < T_s;
-  float acc[8];
+  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+    float acc[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int k = 0; k < K; ++k) {
-    const int32_t r = token_row[t * K + k];
-    if (r < 0) continue;
-    const float wk = w[t * K + k];
-    const i32x4 raw = *reinterpret_cast<const i32x4*>(o + (int64_t)r * ldo + c);
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < n; ++i) {
+      const float wk = sw[i];
+      const i32x4 raw = *reinterpret_cast<const i32x4*>(o + (int64_t)srow[i] * ldo + c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(wk, bf16_to_f32((uint32_t)raw[i] & 0xffffu), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(wk, bf16_to_f32((uint32_t)raw[i] >> 16), acc[2 * i + 1]);
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(wk, bf16_to_f32((uint32_t)raw[q] & 0xffffu), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(wk, bf16_to_f32((uint32_t)raw[q] >> 16), acc[2 * q + 1]);
+      }
     }
-  }
-  if (shared) {
-    const i32x4 raw = *reinterpret_cast<const i32x4*>(s + t * lds + c);
+    if (shared) {
+      const i32x4 raw = *reinterpret_cast<const i32x4*>(s + t * lds + c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += bf16_to_f32((uint32_t)raw[i] & 0xffffu);
-      acc[2 * i + 1] += bf16_to_f32((uint32_t)raw[i] >> 16);
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_to_f32((uint32_t)raw[q] & 0xffffu);
+        acc[2 * q + 1] += bf16_to_f32((uint32_t)raw[q] >> 16);
+      }
     }
-  }
-  i32x4 out;
+    i32x4 out;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = (int)pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-  *reinterpret_cast<i32x4*>(y + t * ldy + c) = out;
+    for (int q = 0; q < 4; ++q) out[q] = (int)pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    *reinterpret_cast<i32x4*>(y + t * ldy + c) = out;
+  }
 }
 
 hipError_t launch_combine(const uint16_t* o, int64_t ldo, const int32_t* token_row, const float* w,
                           const uint16_t* s, int64_t lds, int T_s, int T, int K, int H, uint16_t* y, int64_t ldy,
                           hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((unsigned)T, (unsigned)ceil_div(H, 1024));
-  combine_kernel<<<grid, 128, 0, stream>>>(o, ldo, token_row, w, s, lds, T_s, K, H, y, ldy);
+  const int threads = (int)std::min<int64_t>(1024, round_up(ceil_div(H, 8), 64));
+  combine_kernel<<<(unsigned)T, threads, 0, stream>>>(o, ldo, token_row, w, s, lds, T_s, K, H, y, ldy);
   return hipGetLastError();
 }
 

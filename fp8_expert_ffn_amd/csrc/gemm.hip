@@ -75,7 +75,8 @@ constexpr int kModeBF16 = 0, kModeFP8X = 1, kModeFP8 = 2;
 // 32 * NT weight rows (gate/up: 16 * NT gate + 16 * NT up rows, i.e. 16 * NT
 // columns of h; down: 32 * NT columns of o). Wave (wm, wn) computes rows
 // [64 wm, 64 wm + 64) x 16 * NT weight rows as 4 x NT MFMA tiles of 16x16
-// (NT = 4 by default: two workgroups fit one CU). Operands move global -> LDS
+// (NT = 4 by default: two workgroups fit one CU); a tile with at most 64 rows
+// uses 2 x NT MFMA tiles per wave on rows [32 wm, 32 wm + 32). Operands move global -> LDS
 // with direct (asynchronous, register-free) loads through an NS-stage ring; a
 // stage is 128 bytes of every A and weight row (one 128-wide FP8 scale slice,
 // or 64 BF16 elements) plus the A rows' activation scales. LDS rows are 128
@@ -111,7 +112,7 @@ template <int MODE, bool GATEUP, int NS, int NT>
 __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gemm_tile_kernel(const TileArgs p,
                                                                                               int nNB, int n_valid) {
   constexpr bool kScaled = MODE != kModeBF16;
-  constexpr int MT = 4, NH = NT / 2;   // gate/up: NH gate subtiles, then NH up subtiles per wave
+  constexpr int NH = NT / 2;           // gate/up: NH gate subtiles, then NH up subtiles per wave
   constexpr int kRowsB = 32 * NT;      // weight rows per workgroup
   constexpr int kRows = kBM + kRowsB;  // A rows, then weight rows
   constexpr int kInstA = kBM / 32, kInstB = kRowsB / 32;  // direct copies per wave per stage
@@ -231,162 +232,170 @@ __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gem
     if (kScaled && wave < 2) lds_copy4(p.a_scales + srcS + s, scale_ptr(uc) + 64 * wave);
   };
 
-  f32x4 acc[MT][NT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // A tile of at most 64 rows (the last tile of a group) runs with 2 row
+  // subtiles per wave (wave rows 32 wm .. 32 wm + 31) instead of 4, halving its
+  // MFMA and conversion work; the copies are the same.
+  auto run = [&](auto mtc) {
+    constexpr int MT = decltype(mtc)::value;
+    f32x4 acc[MT][NT];
+  #pragma unroll
+    for (int i = 0; i < MT; ++i)
+  #pragma unroll
+      for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // weight rows (within the weight region) of this lane's subtiles; the
-  // weight fragment is the first MFMA operand, the A fragment the second
-  auto brow = [&](int j) -> int {
-    if (GATEUP) return (j < NH ? 0 : 16 * NT) + wn * 16 * NH + 16 * (j % NH) + r16;
-    return wn * 16 * NT + 16 * j + r16;
-  };
+    // weight rows (within the weight region) of this lane's subtiles; the
+    // weight fragment is the first MFMA operand, the A fragment the second
+    auto brow = [&](int j) -> int {
+      if (GATEUP) return (j < NH ? 0 : 16 * NT) + wn * 16 * NH + 16 * (j % NH) + r16;
+      return wn * 16 * NT + 16 * j + r16;
+    };
 
-  auto compute = [&](auto uc, int s) {
-    const uint8_t* st = stage_ptr(uc);
-    const float* lsa = scale_ptr(uc);
-    i32x4 fa[MT][2];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int row = 64 * wm + 16 * i + r16;
-      fa[i][0] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4));
-      fa[i][1] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4 + 1));
-    }
-    // a_scale * w_scale of this stage's slice for the lane's row of each
-    // subtile (index 0: gate or down weights, 1: up weights)
-    float saw[GATEUP ? 2 : 1][MT];
-    if constexpr (kScaled) {
-      const float w0s = GATEUP ? lsw[0][s] : lsw[wn][s];
-      const float w1s = GATEUP ? lsw[1][s] : 0.f;
-#pragma unroll
+    auto compute = [&](auto uc, int s) {
+      const uint8_t* st = stage_ptr(uc);
+      const float* lsa = scale_ptr(uc);
+      i32x4 fa[MT][2];
+  #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const float a = lsa[64 * wm + 16 * i + r16];
-        saw[0][i] = a * w0s;
-        if constexpr (GATEUP) saw[GATEUP ? 1 : 0][i] = a * w1s;
+        const int row = 16 * MT * wm + 16 * i + r16;
+        fa[i][0] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4));
+        fa[i][1] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4 + 1));
       }
-    }
-    if constexpr (MODE == kModeFP8X) {
-      // exact products: codes -> BF16, four 16x16x32 MFMAs per 128-wide slice
-      i32x4 a16[MT][4];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        e4m3x16_to_bf16(fa[i][0], a16[i][0], a16[i][1]);
-        e4m3x16_to_bf16(fa[i][1], a16[i][2], a16[i][3]);
-      }
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int bj = brow(j);
-        const uint8_t* bp = st + (kBM + bj) * 128;
-        const i32x4 b0 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4));
-        const i32x4 b1 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1));
-        i32x4 b16[4];
-        e4m3x16_to_bf16(b0, b16[0], b16[1]);
-        e4m3x16_to_bf16(b1, b16[2], b16[3]);
-        const int wsel = (GATEUP && j >= NH) ? 1 : 0;
-#pragma unroll
+      // a_scale * w_scale of this stage's slice for the lane's row of each
+      // subtile (index 0: gate or down weights, 1: up weights)
+      float saw[GATEUP ? 2 : 1][MT];
+      if constexpr (kScaled) {
+        const float w0s = GATEUP ? lsw[0][s] : lsw[wn][s];
+        const float w1s = GATEUP ? lsw[1][s] : 0.f;
+  #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4)
-            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b16[k4]),
-                                                           __builtin_bit_cast(bf16x8, a16[i][k4]), part, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[r], saw[wsel][i], acc[i][j][r]);
+          const float a = lsa[16 * MT * wm + 16 * i + r16];
+          saw[0][i] = a * w0s;
+          if constexpr (GATEUP) saw[GATEUP ? 1 : 0][i] = a * w1s;
         }
       }
-    } else if constexpr (MODE == kModeFP8) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int bj = brow(j);
-        const uint8_t* bp = st + (kBM + bj) * 128;
-        const i32x4 b0 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4));
-        const i32x4 b1 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1));
-        const i32x8 b8 = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        const int wsel = (GATEUP && j >= NH) ? 1 : 0;
-#pragma unroll
+      if constexpr (MODE == kModeFP8X) {
+        // exact products: codes -> BF16, four 16x16x32 MFMAs per 128-wide slice
+        i32x4 a16[MT][4];
+  #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          const i32x8 a8 = i32x8{fa[i][0][0], fa[i][0][1], fa[i][0][2], fa[i][0][3],
-                                 fa[i][1][0], fa[i][1][1], fa[i][1][2], fa[i][1][3]};
-          const f32x4 pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                             0, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pr[r], saw[wsel][i], acc[i][j][r]);
+          e4m3x16_to_bf16(fa[i][0], a16[i][0], a16[i][1]);
+          e4m3x16_to_bf16(fa[i][1], a16[i][2], a16[i][3]);
         }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int bj = brow(j);
-        const uint8_t* bp = st + (kBM + bj) * 128;
-        const i32x4 b0 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4));
-        const i32x4 b1 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1));
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b0),
-                                                              __builtin_bit_cast(bf16x8, fa[i][0]), acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b1),
-                                                              __builtin_bit_cast(bf16x8, fa[i][1]), acc[i][j], 0, 0, 0);
+  #pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int bj = brow(j);
+          const uint8_t* bp = st + (kBM + bj) * 128;
+          const i32x4 b0 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4));
+          const i32x4 b1 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1));
+          i32x4 b16[4];
+          e4m3x16_to_bf16(b0, b16[0], b16[1]);
+          e4m3x16_to_bf16(b1, b16[2], b16[3]);
+          const int wsel = (GATEUP && j >= NH) ? 1 : 0;
+  #pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4)
+              part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b16[k4]),
+                                                             __builtin_bit_cast(bf16x8, a16[i][k4]), part, 0, 0, 0);
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[r], saw[wsel][i], acc[i][j][r]);
+          }
         }
-      }
-    }
-  };
-
-  // ---- NS-stage pipeline: stage s lives in buffer s % NS ----
-  constexpr int kCopies = kInstA + kInstB;  // per wave per stage, plus one scale copy on waves 0 and 1
-  const int S = p.stages;
-  const bool scale_wave = kScaled && wave < 2;
-  static_for<0, NS - 1>([&](auto uc) {
-    if (decltype(uc)::value < S) issue(uc, decltype(uc)::value);
-  });
-  for (int s0 = 0; s0 < S; s0 += NS) {
-    static_for<0, NS>([&](auto uc) {
-      constexpr int u = decltype(uc)::value;
-      const int s = s0 + u;
-      if (s < S) {
-        if (s + NS - 1 < S) {
-          issue(std::integral_constant<int, (u + NS - 1) % NS>{}, s + NS - 1);
-          // stage s is complete once at most the NS-1 younger stages are in flight
-          if (scale_wave) wait_vmcnt<(kCopies + 1) * (NS - 1)>();
-          else wait_vmcnt<kCopies * (NS - 1)>();
-        } else {
-          wait_vmcnt<0>();
+      } else if constexpr (MODE == kModeFP8) {
+  #pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int bj = brow(j);
+          const uint8_t* bp = st + (kBM + bj) * 128;
+          const i32x4 b0 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4));
+          const i32x4 b1 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1));
+          const i32x8 b8 = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+          const int wsel = (GATEUP && j >= NH) ? 1 : 0;
+  #pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const i32x8 a8 = i32x8{fa[i][0][0], fa[i][0][1], fa[i][0][2], fa[i][0][3],
+                                   fa[i][1][0], fa[i][1][1], fa[i][1][2], fa[i][1][3]};
+            const f32x4 pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                               0, 0, 0, 0);
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pr[r], saw[wsel][i], acc[i][j][r]);
+          }
         }
-        stage_barrier();  // every wave's copies of stage s have landed in LDS
-        if (active) compute(uc, s);
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
-        stage_barrier();  // buffer u may be refilled
-      }
-    });
-  }
-
-  if (!active) return;
-  // ---- epilogue: the weight fragment is the MFMA's first operand, so lane
-  // (r16, g4) holds row 16 i + r16 and the 4 consecutive columns 16 j + 4 g4 + r
-  // of each 16x16 tile: one 8-byte store per tile when the output allows it.
-  const bool wide = (p.ldo & 3) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 7) == 0;
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int m = m0 + 64 * wm + 16 * i + r16;
-    if (m >= m_end) continue;
-    uint16_t* orow = p.out + (int64_t)m * p.ldo + wcol0 + 4 * g4;
-#pragma unroll
-    for (int j = 0; j < (GATEUP ? NH : NT); ++j) {
-      float v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = GATEUP ? silu(acc[i][j][r]) * acc[i][j + NH][r] : acc[i][j][r];
-      const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-      if (wide) {
-        *reinterpret_cast<uint2*>(orow + 16 * j) = make_uint2(lo, hi);
       } else {
-        orow[16 * j] = (uint16_t)lo;
-        orow[16 * j + 1] = (uint16_t)(lo >> 16);
-        orow[16 * j + 2] = (uint16_t)hi;
-        orow[16 * j + 3] = (uint16_t)(hi >> 16);
+  #pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int bj = brow(j);
+          const uint8_t* bp = st + (kBM + bj) * 128;
+          const i32x4 b0 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4));
+          const i32x4 b1 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1));
+  #pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b0),
+                                                                __builtin_bit_cast(bf16x8, fa[i][0]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b1),
+                                                                __builtin_bit_cast(bf16x8, fa[i][1]), acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    };
+
+    // ---- NS-stage pipeline: stage s lives in buffer s % NS ----
+    constexpr int kCopies = kInstA + kInstB;  // per wave per stage, plus one scale copy on waves 0 and 1
+    const int S = p.stages;
+    const bool scale_wave = kScaled && wave < 2;
+    static_for<0, NS - 1>([&](auto uc) {
+      if (decltype(uc)::value < S) issue(uc, decltype(uc)::value);
+    });
+    for (int s0 = 0; s0 < S; s0 += NS) {
+      static_for<0, NS>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        const int s = s0 + u;
+        if (s < S) {
+          if (s + NS - 1 < S) {
+            issue(std::integral_constant<int, (u + NS - 1) % NS>{}, s + NS - 1);
+            // stage s is complete once at most the NS-1 younger stages are in flight
+            if (scale_wave) wait_vmcnt<(kCopies + 1) * (NS - 1)>();
+            else wait_vmcnt<kCopies * (NS - 1)>();
+          } else {
+            wait_vmcnt<0>();
+          }
+          stage_barrier();  // every wave's copies of stage s have landed in LDS
+          if (active) compute(uc, s);
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
+          stage_barrier();  // buffer u may be refilled
+        }
+      });
+    }
+
+    if (!active) return;
+    // ---- epilogue: the weight fragment is the MFMA's first operand, so lane
+    // (r16, g4) holds row 16 i + r16 and the 4 consecutive columns 16 j + 4 g4 + r
+    // of each 16x16 tile: one 8-byte store per tile when the output allows it.
+    const bool wide = (p.ldo & 3) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 7) == 0;
+  #pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int m = m0 + 16 * MT * wm + 16 * i + r16;
+      if (m >= m_end) continue;
+      uint16_t* orow = p.out + (int64_t)m * p.ldo + wcol0 + 4 * g4;
+  #pragma unroll
+      for (int j = 0; j < (GATEUP ? NH : NT); ++j) {
+        float v[4];
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = GATEUP ? silu(acc[i][j][r]) * acc[i][j + NH][r] : acc[i][j][r];
+        const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+        if (wide) {
+          *reinterpret_cast<uint2*>(orow + 16 * j) = make_uint2(lo, hi);
+        } else {
+          orow[16 * j] = (uint16_t)lo;
+          orow[16 * j + 1] = (uint16_t)(lo >> 16);
+          orow[16 * j + 2] = (uint16_t)hi;
+          orow[16 * j + 3] = (uint16_t)(hi >> 16);
+        }
       }
     }
-  }
+  };
+  if (m_end - m0 <= 64) run(std::integral_constant<int, 2>{});
+  else run(std::integral_constant<int, 4>{});
 }
 
 __global__ void fill_offsets_kernel(int32_t* offsets, int rows) {

@@ -196,7 +196,8 @@ dmoe_status dmoe_shared_expert(int32_t dtype, const void* a, int64_t lda, const 
  *   y[t] = bf16( sum_{k=0..K-1, token_row[t,k] >= 0} topk_w[t,k] * o[token_row[t,k]]
  *                + (t < T_s ? s_out[t] : 0) ),
  * accumulated in FP32 in slot order, no atomics. s_out may be NULL (T_s
- * ignored). o: [*, ldo] BF16; y: [T, ldy] BF16.
+ * ignored). o: [*, ldo] BF16; y: [T, ldy] BF16. Requires 1 <= K <= 64 and
+ * H % 8 == 0.
  */
 dmoe_status dmoe_combine(const uint16_t* o, int64_t ldo, const int32_t* token_row, const float* topk_w,
                          const uint16_t* s_out, int64_t lds, int32_t T_s, int32_t T, int32_t K, int32_t H,

@@ -95,3 +95,12 @@ def test_forward_desc_validation_and_sizes(L):
     ptrs = L.LayerPtrs()
     st = lib.dmoe_forward(ctypes.byref(bf), ctypes.byref(ptrs), None, 0, None)
     assert st == L._lib.DMOE_ERR_INVALID_ARG  # x is NULL; rejected before any launch
+
+
+def test_combine_rejects_bad_slot_count_and_width(L):
+    lib = L.lib()
+    f = 0x1000
+    assert lib.dmoe_combine(f, 5120, f, f, None, 0, 0, 64, 65, 5120, f, 5120, None) == L._lib.DMOE_ERR_INVALID_ARG
+    assert b"K = 65" in lib.dmoe_last_error()
+    assert lib.dmoe_combine(f, 5120, f, f, None, 0, 0, 64, 8, 5124, f, 5124, None) == L._lib.DMOE_ERR_INVALID_ARG
+    assert lib.dmoe_combine(None, 5120, None, None, None, 0, 0, 0, 8, 5120, None, 5120, None) == 0  # T == 0
