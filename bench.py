@@ -134,8 +134,10 @@ def accounting(cfg, offsets: np.ndarray, logits_computed: bool) -> dict:
                 gu_rows=gu_rows)
 
 
-def cpu_baseline(cfg, x_bits, wr, given, seconds: float) -> dict:
-    """The oracle, as it stands, on a bounded sample of the same workload's tokens."""
+def cpu_baseline(cfg, x_bits, wr, given, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same workload's tokens.
+
+    Returns the baseline record and the oracle's results (one per sampled batch) for the parity check."""
     import oracle
     import synth
     try:
@@ -147,19 +149,51 @@ def cpu_baseline(cfg, x_bits, wr, given, seconds: float) -> dict:
         (lambda w, e: synth.expert_weight_bf16(cfg, w, e))
     rng = np.random.default_rng(7)
     done, n, t0 = 0, 2, time.perf_counter()
+    results = []
     while True:
         tok = np.sort(rng.choice(cfg.T, size=min(n, cfg.T), replace=False))
-        oracle.moe_forward(cfg, x_bits, get, w_r=wr, logits=given, tokens=tok)
+        results.append(oracle.moe_forward(cfg, x_bits, get, w_r=wr, logits=given, tokens=tok))
         done += tok.size
         el = time.perf_counter() - t0
         if el >= seconds or done >= cfg.T:
             break
         n = min(cfg.T, max(1, int(tok.size * max(1.0, (seconds - el) / max(el, 1e-3)) * 0.5)))
-    return {"value": done / el, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"{done} tokens of the {cfg.name} workload (random token subsets, each token's full "
-                      f"layer output incl. per-expert weight preparation), {el:.1f}s on "
-                      f"{platform.processor() or platform.machine()}; BLAS threads {blas}, elementwise NumPy "
-                      f"single-threaded"}
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
+    rec = {"value": done / el, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+           "host_cpu_count": os.cpu_count(), "host_affinity": affinity,
+           "sample": f"{done} tokens of the {cfg.name} workload (random token subsets, each token's full "
+                     f"layer output incl. per-expert weight preparation), {el:.1f}s on "
+                     f"{platform.processor() or platform.machine()}; BLAS threads {blas}, elementwise NumPy "
+                     f"single-threaded"}
+    return rec, results
+
+
+def sample_parity(cfg, results, y_gpu: np.ndarray, ids_gpu: np.ndarray) -> dict:
+    """GPU output of the timed layer against the oracle on the cpu_baseline's sampled tokens. Tokens whose top-K
+    set differs (router near-ties between the GPU's FP32 logits and the oracle's) are left out and counted."""
+    tok = np.concatenate([r.tokens for r in results])
+    y_or = np.concatenate([r.y for r in results])
+    ids_or = np.concatenate([r.ids for r in results])
+    same = np.all(np.sort(ids_gpu[tok], 1) == np.sort(ids_or, 1), axis=1)
+    yg, yo = y_gpu[tok][same], y_or[same]
+    if yo.size == 0:
+        return {"tokens": 0}
+    rms = float(np.sqrt(np.mean(yo ** 2)))
+    err = np.abs(yg - yo)
+    # both sides are BF16 roundings, so one element may differ by one BF16 ulp of itself on top of 2e-2 RMS
+    a = np.abs(yo)
+    ulp = np.where(a > 0, np.ldexp(1.0, np.maximum(np.frexp(a)[1] - 8, -133)), 0.0)
+    worst = float(np.max(err / np.maximum(2e-2 * rms + ulp, 1e-300)))
+    rel = float(np.linalg.norm(yg - yo) / max(np.linalg.norm(yo), 1e-300))
+    over = float(np.mean(err > 2e-2 * rms))
+    return {"tokens": int(same.sum()), "routing_near_ties_skipped": int((~same).sum()),
+            "rel_l2": rel, "max_abs_over_rms": float(err.max() / max(rms, 1e-300)),
+            "frac_over_2e-2_rms": over, "max_err_over_bound": worst,
+            "pass": bool(rel <= 5e-3 and worst <= 1.0 and over <= 1e-2),
+            "bound": "rel_l2 <= 5e-3; per element |dy| <= 2e-2 RMS + 1 BF16 ulp; <= 1% of elements over 2e-2 RMS"}
 
 
 def main() -> int:
@@ -235,6 +269,8 @@ def main() -> int:
     h1 = time.perf_counter()
     ms_step = start.elapsed_time(end) / args.steps
     gu_ms = float(np.mean([ev[i][gu].elapsed_time(ev[i][gu + 1]) for i in range(args.steps)]))
+    # per-step layer times: from one step's gate/up start to the next one's (no extra markers)
+    step_ms = np.array([ev[i][gu].elapsed_time(ev[i + 1][gu]) for i in range(args.steps - 1)])
     log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (host {1e3 * (h1 - h0) / args.steps:.4f} ms/step), "
         f"gate/up launch {gu_ms:.4f} ms")
 
@@ -283,6 +319,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)]
+        if step_ms.size else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -301,7 +339,10 @@ def main() -> int:
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, x_bits, wr, given, args.cpu_seconds)
+        result["cpu_baseline"], results = cpu_baseline(cfg, x_bits, wr, given, args.cpu_seconds)
+        y_gpu = out["y"].view(torch.int16).cpu().numpy().view(np.uint16)
+        y_gpu = (y_gpu.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        result["parity_sample"] = sample_parity(cfg, results, y_gpu, out["topk_ids"].cpu().numpy())
     print(json.dumps(result), flush=True)
     return 0
 
