@@ -82,7 +82,6 @@ __device__ __forceinline__ int64_t a_row(const TileArgs& p, const GroupView& v, 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
 
 __device__ __forceinline__ void e4m3x16_to_bf16(const i32x4 src, i32x4& lo, i32x4& hi) {
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   int out[8];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -106,17 +105,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Asynchronous global -> LDS copies of 16 (or 4) bytes per lane: lane l writes
 // LDS bytes [base + 16 l, +16) (resp. [base + 4 l, +4)); base is wave-uniform
-// and goes through M0. Issued from asm so that the compiler's wait insertion,
-// which cannot tell the pipeline's LDS buffers apart, does not make every LDS
-// read wait for every copy in flight; the pipeline waits on vmcnt itself. The
-// instruction writes no register, so nothing of it is live after issue.
+// and is passed in M0 (an input operand bound to that register, so the
+// compiler sets M0 itself and knows it is read). Issued from asm so that the
+// compiler's wait insertion, which cannot tell the pipeline's LDS buffers
+// apart, does not make every LDS read wait for every copy in flight; the
+// pipeline waits on vmcnt itself. The instruction writes no register, so
+// nothing of it is live after issue.
 __device__ __forceinline__ void lds_copy16(const void* gptr, const void* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0) : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
 }
 __device__ __forceinline__ void lds_copy4(const void* gptr, const void* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(m0) : "memory", "m0");
+  asm volatile("global_load_lds_dword %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
 }
 
 // Workgroup barrier without the memory fence of __syncthreads (whose release

@@ -75,7 +75,6 @@ __global__ __launch_bounds__(64 * NW) void router_logits_kernel(const uint16_t* 
 #pragma unroll
     for (int j = 0; j < EE; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll 4
   for (int k = kbeg; k < kbeg + kq; k += 32) {
     bf16x8 a[TT];
 #pragma unroll
