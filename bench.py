@@ -202,7 +202,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=1, help="workload index (0 tiny, 1 decode, 2 prefill, "
-                                                                "3 EP share, 4 non-divisible)")
+                                                                "3 EP share, 4 non-divisible, 5 vision BF16, "
+                                                                "6 vision FP8, 7 dense FFN FP8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -17,6 +17,7 @@ regenerated without drawing the others. Draws:
 * ``down``     -- N(0, 1/sqrt(F)) in float32, ``[H, F]`` per expert.
 * skewed logits (EP8 share) -- ``-1.1*ln(e+1) + N(0,1)`` in float64, stored as float32.
 * uniform logits (non-divisible stress) -- U[-4, 4) in float64, stored as float32.
+* single logits (dense layer as one expert) -- zeros.
 
 BF16 workloads store the weights as bfloat16 (round to nearest even of the
 float32 draw); FP8 workloads keep the float32 draw, which each consumer
@@ -48,7 +49,8 @@ class LayerConfig:
     T tokens of width H; E routed experts of which this GPU holds E_loc starting
     at e0; top-K routing; routed FFN width F; shared FFN width F_s applied to
     tokens [0, T_s). ``logits`` says where the router logits come from:
-    "router" (x @ W_r^T), "zipf" (skewed, given) or "uniform" (given).
+    "router" (x @ W_r^T), "zipf" (skewed, given), "uniform" (given) or
+    "single" (given zeros, for E = K = 1).
     """
     name: str
     T: int
@@ -83,6 +85,17 @@ CONFIGS = [
                 dtype="fp8", T_s=2048, logits="zipf"),
     LayerConfig("nondiv_fp8", T=2048, H=5120, F=1400, F_s=1400, E=256, E_loc=256, e0=0, K=8,
                 dtype="fp8", T_s=2048, logits="uniform"),
+    # Vision-tower MoE (Transformers docs "Dots3Note", Dots3NoteVisionConfig: hidden_size 1536,
+    # moe_intermediate_size 2112, num_local_experts 64, FP32 router; no shared expert). The docs leave
+    # num_experts_per_tok unset; the text model's top-8 is used. 2112 = 16.5 x 128: a partial FP8 block.
+    LayerConfig("vision_bf16", T=4096, H=1536, F=2112, F_s=0, E=64, E_loc=64, e0=0, K=8,
+                dtype="bf16", T_s=0, logits="router"),
+    LayerConfig("vision_fp8", T=4096, H=1536, F=2112, F_s=0, E=64, E_loc=64, e0=0, K=8,
+                dtype="fp8", T_s=0, logits="router"),
+    # Dense first-layer FFN (Dots3NoteTextConfig intermediate_size 13824) as one expert with top-1:
+    # every token's single routing weight is exactly 1, so y is the dense SwiGLU FFN output.
+    LayerConfig("dense_fp8", T=4096, H=5120, F=13824, F_s=0, E=1, E_loc=1, e0=0, K=1,
+                dtype="fp8", T_s=0, logits="single"),
 ]
 
 
@@ -137,6 +150,8 @@ def given_logits(cfg: LayerConfig) -> np.ndarray:
         return (bias[None, :] + g.standard_normal((cfg.T, cfg.E))).astype(np.float32)
     if cfg.logits == "uniform":
         return g.uniform(-4.0, 4.0, size=(cfg.T, cfg.E)).astype(np.float32)
+    if cfg.logits == "single":
+        return np.zeros((cfg.T, cfg.E), dtype=np.float32)
     raise ValueError(f"workload {cfg.name} computes its logits from x")
 
 

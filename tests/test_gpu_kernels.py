@@ -68,6 +68,38 @@ def test_router_logits(T, H, E):
     assert err <= LOGIT_TOL
 
 
+def test_vision_router_near_ties_need_fp32():
+    """Vision-router shape (hidden 1536, 64 experts, top-8) with experts in near-duplicate triples, so that the
+    top-8 boundary (8 = 2 triples + 2) falls inside a triple whose logits are ~1e-3 apart. The FP32 router must
+    pick exactly the oracle's experts wherever the decisive gap exceeds 4x the logit tolerance, while a router
+    with BF16-rounded weights picks differently on some of those tokens (the precision the FP32 router exists
+    for)."""
+    T, H, E, K = 512, 1536, 64, 8
+    rng = np.random.default_rng(2112)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    w = rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.02)
+    for g in range(E // 3):  # experts 3g+1, 3g+2 are small perturbations of expert 3g
+        for j in (1, 2):
+            w[3 * g + j] = w[3 * g] + rng.standard_normal(H, dtype=np.float32) * np.float32(0.02 * 2.0 ** -10)
+    x64 = oracle.bf16_to_f64(x)
+    L_ref = oracle.router_logits(x64, w)
+    ids_ref, _ = oracle.route(L_ref, K)
+    L_gpu = dm.dmoe_router_logits(to_dev_bf16(x), torch.from_numpy(w).to(DEV))
+    ids_gpu, _ = dm.dmoe_route(L_gpu, K)
+    ids_gpu = ids_gpu.cpu().numpy()
+    srt = np.sort(L_ref.astype(np.float64), axis=1)[:, ::-1]
+    gap = srt[:, K - 1] - srt[:, K]
+    robust = gap > 4 * LOGIT_TOL
+    same = np.all(np.sort(ids_gpu, 1) == np.sort(ids_ref, 1), axis=1)
+    say(f"  near-tie tokens (gap < 1e-3): {(gap < 1e-3).sum()}, robust {robust.sum()}, "
+        f"GPU differs on {(~same).sum()} (all non-robust: {np.all(~robust[~same])})")
+    assert np.all(same[robust])
+    ids_bf, _ = oracle.route(oracle.router_logits(x64, synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(w))), K)
+    bf_diff = ~np.all(np.sort(ids_bf, 1) == np.sort(ids_ref, 1), axis=1)
+    say(f"  a BF16-weight router differs on {bf_diff.sum()} tokens, {(bf_diff & robust).sum()} of them robust")
+    assert (bf_diff & robust).sum() > 0
+
+
 # --------------------------------------------------------------------------- permute
 
 def _permute_case(ids: np.ndarray, e0: int, e_loc: int):

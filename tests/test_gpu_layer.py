@@ -29,6 +29,16 @@ CASES = {
                                            dtype="bf16", T_s=50, logits="uniform"),
     "single_token_fp8": synth.LayerConfig("one_tok", T=1, H=512, F=128, F_s=128, E=16, E_loc=16, e0=0, K=4,
                                           dtype="fp8", T_s=1, logits="router"),
+    # vision-tower MoE shape (hidden 1536, FFN 2112 = 16.5 blocks, 64 experts, no shared expert)
+    "vision_small_bf16": synth.LayerConfig("vision_small", T=256, H=1536, F=2112, F_s=0, E=64, E_loc=64, e0=0,
+                                           K=8, dtype="bf16", T_s=0, logits="router"),
+    "vision_small_fp8": synth.LayerConfig("vision_small_fp8", T=256, H=1536, F=2112, F_s=0, E=64, E_loc=64, e0=0,
+                                          K=8, dtype="fp8", T_s=0, logits="router"),
+    # dense FFN as one expert with top-1 (routing weight exactly 1)
+    "dense_small_fp8": synth.LayerConfig("dense_small", T=192, H=1024, F=13824, F_s=0, E=1, E_loc=1, e0=0, K=1,
+                                         dtype="fp8", T_s=0, logits="single"),
+    "dense_small_bf16": synth.LayerConfig("dense_small_bf16", T=100, H=512, F=2304, F_s=0, E=1, E_loc=1, e0=0,
+                                          K=1, dtype="bf16", T_s=0, logits="single"),
 }
 
 
