@@ -217,24 +217,43 @@ def router_logits(x: np.ndarray, w_r: np.ndarray) -> np.ndarray:
     return (np.asarray(x, dtype=np.float64) @ np.asarray(w_r, dtype=np.float64).T).astype(np.float32)
 
 
-def route(logits: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
-    """Top-k routing with renormalised softmax weights.
+def route(logits: np.ndarray, k: int, n_group: int = 1, topk_group: int | None = None,
+          renormalize: bool = True, scaling: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
+    """Top-k routing with softmax weights.
 
     Selection: the k largest FP32 logits; equal values go to the lower expert
     index; -0.0 is treated as +0.0; slot j holds the expert of rank j.
-    Weights: p = softmax over all experts (float64), then p_S / sum(p_S) over
-    the selected set S (``norm_topk_prob``), times ``routed_scaling_factor`` 1.0,
-    stored as float32. parity pinned (brute force, closed forms).
+    Group-limited selection (Transformers docs "Dots3Note", Dots3NoteTextConfig
+    ``n_group``, ``topk_group``; 1 and 1 by default, i.e. ungrouped): the E
+    experts form n_group groups of E/n_group consecutive experts, a group's
+    score is its largest logit (the docs fix only that the chosen experts lie
+    in topk_group groups; the best expert of a group is the plainest score),
+    the topk_group groups with the largest scores are kept (equal scores: the
+    lower group), and the k experts are the top-k of the kept groups' experts.
+    Weights: p = softmax over all E experts (float64); with ``renormalize``
+    (``norm_topk_prob``, default true) p_S / sum(p_S) over the selected set S,
+    otherwise p_S; times ``scaling`` (``routed_scaling_factor``, default 1.0);
+    stored as float32. parity pinned (brute force, closed forms, hand example).
     """
     L = np.asarray(logits, dtype=np.float32)
     L = np.where(L == 0, np.float32(0.0), L)  # canonicalise -0.0
-    order = np.argsort(-L, axis=1, kind="stable")  # stable: ties keep ascending expert index
+    T, E = L.shape
+    topk_group = n_group if topk_group is None else topk_group
+    sel = L.astype(np.float64)
+    if n_group > 1:
+        assert E % n_group == 0 and 1 <= topk_group <= n_group and k <= topk_group * (E // n_group)
+        gscore = sel.reshape(T, n_group, E // n_group).max(axis=2)
+        gkeep = np.argsort(-gscore, axis=1, kind="stable")[:, :topk_group]  # ties: lower group first
+        allowed = np.zeros((T, n_group), dtype=bool)
+        np.put_along_axis(allowed, gkeep, True, axis=1)
+        sel = np.where(np.repeat(allowed, E // n_group, axis=1), sel, -np.inf)
+    order = np.argsort(-sel, axis=1, kind="stable")  # stable: ties keep ascending expert index
     ids = order[:, :k].astype(np.int32)
     L64 = L.astype(np.float64)
     ex = np.exp(L64 - L64.max(axis=1, keepdims=True))
     p = ex / ex.sum(axis=1, keepdims=True)
     ps = np.take_along_axis(p, ids.astype(np.int64), axis=1)
-    w = ps / ps.sum(axis=1, keepdims=True) * 1.0  # routed_scaling_factor
+    w = (ps / ps.sum(axis=1, keepdims=True) if renormalize else ps) * float(scaling)
     return ids, w.astype(np.float32)
 
 

@@ -155,3 +155,62 @@ def test_permute_no_local_pairs():
     ids[:, 1] = 41
     off, rt, rs, tr = _check_permutation(ids, 0, 32)
     assert off[-1] == 0 and np.all(tr == -1)
+
+
+# --------------------------------------------------------------------------- routing variants
+
+def _brute_grouped(lrow, k, n_group, topk_group):
+    """Rank the groups by their best logit (ties: lower group), keep topk_group of them, then rank the kept
+    experts with the ungrouped rule; every rank counted explicitly."""
+    l = np.where(lrow == 0, 0.0, lrow.astype(np.float64))
+    E = l.size
+    gs = E // n_group
+    score = [max(l[g * gs:(g + 1) * gs]) for g in range(n_group)]
+    keep = [g for g in range(n_group)
+            if sum((score[h] > score[g]) or (score[h] == score[g] and h < g) for h in range(n_group)) < topk_group]
+    allowed = [e for e in range(E) if e // gs in keep]
+    out = [None] * k
+    for e in allowed:
+        r = sum((l[f] > l[e]) or (l[f] == l[e] and f < e) for f in allowed)
+        if r < k:
+            out[r] = e
+    return np.array(out)
+
+
+def test_grouped_route_hand_example():
+    # groups {0,1} {2,3} {4,5} {6,7}; best logits 0.9, 0.5, 0.8, 0.3 -> keep groups 0 and 2 -> experts {0,1,4,5}
+    L = np.array([[0.1, 0.9, 0.5, 0.4, 0.8, 0.0, 0.3, 0.2]], np.float32)
+    ids, w = oracle.route(L, 3, n_group=4, topk_group=2)
+    np.testing.assert_array_equal(ids, [[1, 4, 0]])          # ungrouped would be [1, 4, 2]
+    e = np.exp(np.array([0.9, 0.8, 0.1], np.float64) - 0.9)
+    np.testing.assert_allclose(w[0], e / e.sum(), rtol=1e-7)
+    # not renormalised: the plain softmax probabilities of the chosen experts, then scaled
+    ids2, w2 = oracle.route(L, 3, n_group=4, topk_group=2, renormalize=False, scaling=2.5)
+    p = scipy.special.softmax(L[0].astype(np.float64))
+    np.testing.assert_array_equal(ids2, ids)
+    np.testing.assert_allclose(w2[0], 2.5 * p[[1, 4, 0]], rtol=1e-7)
+
+
+@pytest.mark.parametrize("E,K,G,TG", [(8, 3, 4, 2), (16, 4, 4, 1), (12, 5, 3, 2), (64, 8, 8, 4), (256, 8, 8, 4)])
+def test_grouped_route_matches_brute_force(E, K, G, TG):
+    rng = np.random.default_rng(E * 31 + G)
+    L = np.concatenate([_adversarial_logits(E, rng), (rng.standard_normal((40, E)) * 1.43).astype(np.float32)])
+    ids, w = oracle.route(L, K, n_group=G, topk_group=TG)
+    for t in range(L.shape[0]):
+        np.testing.assert_array_equal(ids[t], _brute_grouped(L[t], K, G, TG))
+        groups = set(int(e) // (E // G) for e in ids[t])
+        assert len(groups) <= TG
+    assert np.allclose(w.astype(np.float64).sum(1), 1.0, atol=1e-6)
+
+
+def test_grouped_route_degenerate_cases_reduce_to_ungrouped():
+    rng = np.random.default_rng(3)
+    L = (rng.standard_normal((100, 64)) * 1.43).astype(np.float32)
+    base = oracle.route(L, 8)
+    for G in (1, 2, 8, 64):
+        ids, w = oracle.route(L, 8, n_group=G, topk_group=G)   # every group kept
+        np.testing.assert_array_equal(ids, base[0])
+        np.testing.assert_array_equal(w, base[1])
+    # one expert per group: group selection is itself a top-topk_group, then top-k of those
+    ids, _ = oracle.route(L, 4, n_group=64, topk_group=6)
+    np.testing.assert_array_equal(ids, base[0][:, :4])
