@@ -38,7 +38,8 @@ def log(msg: str) -> None:
 def build_layer(cfg, dev):
     import synth
     from fp8_expert_ffn_amd import MoELayer
-    layer = MoELayer(cfg.H, cfg.F, cfg.F_s, cfg.E, cfg.E_loc, cfg.e0, cfg.K, cfg.dtype, dev)
+    layer = MoELayer(cfg.H, cfg.F, cfg.F_s, cfg.E, cfg.E_loc, cfg.e0, cfg.K, cfg.dtype, dev, n_group=cfg.n_group,
+                     topk_group=cfg.topk_group, renormalize=cfg.renormalize, routed_scaling_factor=cfg.scaling)
     bf16 = cfg.dtype == "bf16"
     for which in ("gate", "up", "down"):
         synth.fill_expert_weights(cfg, which, cfg.experts, lambda i, a, w=which: layer.set_weight(w, i, a), bf16)

@@ -88,16 +88,41 @@ dmoe_status dmoe_router_logits(const uint16_t* x, int64_t ldx, const float* w_r,
   return hip_status(launch_router_logits(x, ldx, w_r, T, H, E, logits, stream), "router_logits launch");
 }
 
-dmoe_status dmoe_route(const float* logits, int32_t T, int32_t E, int32_t K, int32_t* topk_ids, float* topk_w,
-                       hipStream_t stream) {
+namespace {
+// Group-limited routing options; n_group 0 or 1 means ungrouped, topk_group 0 means every group.
+dmoe_status check_route_opts(int32_t E, int32_t K, int32_t n_group, int32_t topk_group, float scaling) {
+  const int32_t g = n_group <= 1 ? 1 : n_group;
+  const int32_t tg = topk_group <= 0 ? g : topk_group;
+  REQ(n_group >= 0 && n_group <= 64, DMOE_ERR_INVALID_ARG, "n_group = %d outside [0, 64]", n_group);
+  REQ(E % g == 0, DMOE_ERR_INVALID_ARG, "E = %d is not a multiple of n_group = %d", E, g);
+  REQ(tg >= 1 && tg <= g, DMOE_ERR_INVALID_ARG, "topk_group = %d outside [1, n_group = %d]", topk_group, g);
+  REQ((int64_t)K <= (int64_t)tg * (E / g), DMOE_ERR_INVALID_ARG,
+      "K = %d exceeds the %d experts of topk_group = %d groups", K, tg * (E / g), tg);
+  REQ(scaling > 0.f && scaling < 3.0e38f, DMOE_ERR_INVALID_ARG, "routed_scaling_factor must be positive and finite");
+  return DMOE_OK;
+}
+}  // namespace
+
+dmoe_status dmoe_route_grouped(const float* logits, int32_t T, int32_t E, int32_t K, int32_t n_group,
+                               int32_t topk_group, int32_t renormalize, float routed_scaling_factor,
+                               int32_t* topk_ids, float* topk_w, hipStream_t stream) {
   REQ(T >= 0, DMOE_ERR_INVALID_ARG, "T = %d < 0", T);
   REQ(E >= 1 && E <= 1024, DMOE_ERR_INVALID_ARG, "E = %d outside [1, 1024]", E);
   REQ(K >= 1 && K <= E && K <= 64, DMOE_ERR_INVALID_ARG, "K = %d outside [1, min(E, 64)]", K);
+  TRY(check_route_opts(E, K, n_group, topk_group, routed_scaling_factor));
   if (T == 0) return ok();
   REQ_PTR(logits, "logits");
   REQ_PTR(topk_ids, "topk_ids");
   REQ_PTR(topk_w, "topk_w");
-  return hip_status(launch_route(logits, T, E, K, topk_ids, topk_w, stream), "route launch");
+  const int g = n_group <= 1 ? 1 : n_group;
+  return hip_status(launch_route(logits, T, E, K, g, topk_group <= 0 ? g : topk_group, renormalize != 0,
+                                 routed_scaling_factor, topk_ids, topk_w, stream),
+                    "route launch");
+}
+
+dmoe_status dmoe_route(const float* logits, int32_t T, int32_t E, int32_t K, int32_t* topk_ids, float* topk_w,
+                       hipStream_t stream) {
+  return dmoe_route_grouped(logits, T, E, K, 1, 1, 1, 1.0f, topk_ids, topk_w, stream);
 }
 
 size_t dmoe_permute_ws_bytes(int32_t T, int32_t K, int32_t E_loc) {
@@ -412,6 +437,8 @@ dmoe_status check_desc(const dmoe_layer_desc* d) {
   REQ(d->dtype != DMOE_FP8_E4M3 || (d->H <= 16384 && d->F <= 16384 && d->F_s <= 16384), DMOE_ERR_UNSUPPORTED,
       "FP8 layers support H, F, F_s up to 16384");
   REQ((int64_t)d->T * d->K <= INT32_MAX / 2, DMOE_ERR_INVALID_ARG, "T*K too large");
+  TRY(check_route_opts(d->E, d->K, d->n_group, d->topk_group,
+                       d->routed_scaling_factor == 0.f ? 1.f : d->routed_scaling_factor));
   return DMOE_OK;
 }
 }  // namespace
@@ -491,7 +518,13 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
   if (!d->logits_given)
     STEP(launch_router_logits(p->x, p->ldx, p->w_router, d->T, d->H, d->E, p->logits, stream), "router_logits");
   STEP(mark(), "event");
-  STEP(launch_route(p->logits, d->T, d->E, d->K, p->topk_ids, p->topk_w, stream), "route");
+  {
+    const int g = d->n_group <= 1 ? 1 : d->n_group;
+    STEP(launch_route(p->logits, d->T, d->E, d->K, g, d->topk_group <= 0 ? g : d->topk_group,
+                      d->no_renormalize == 0, d->routed_scaling_factor == 0.f ? 1.f : d->routed_scaling_factor,
+                      p->topk_ids, p->topk_w, stream),
+         "route");
+  }
   STEP(mark(), "event");
   STEP(launch_permute(p->topk_ids, d->T, d->K, d->e0, d->E_loc, offsets, row_token, row_slot, token_row,
                       at(W_PERM), stream),

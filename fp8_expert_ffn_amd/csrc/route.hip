@@ -1,5 +1,5 @@
-// Router: FP32 logits on matrix cores, then top-K selection and renormalised
-// softmax weights, one wavefront per token.
+// Router: FP32 logits on matrix cores, then top-K selection (optionally
+// group-limited) and softmax weights, one wavefront per token.
 //
 // FP32 routing: Transformers PR #47844, implementation list. Top-K with
 // renormalised weights: Transformers docs "Dots3Note", Dots3NoteTextConfig
@@ -166,9 +166,67 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float(b);
 }
 
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t o = shfl_xor_u64(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += shfl_xor_f64(v, off);
+  return v;
+}
+
+// Group-limited selection (n_group > 1): the experts form n_group groups of
+// E / n_group consecutive experts; a group's score is its best key (largest
+// logit, lower expert first), the topk_group best groups are kept (equal best
+// logits: the lower expert, hence the lower group) and the keys of every other
+// group's experts are cleared, so the K rounds below choose only among kept
+// experts.
+template <int VPL>
+__device__ __forceinline__ void keep_best_groups(uint64_t (&key)[VPL], int lane, int E, int n_group, int topk_group) {
+  const int gs = E / n_group;
+  uint64_t gkey = 0;  // lane g < n_group: best key of group g
+  for (int g = 0; g < n_group; ++g) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && e / gs == g && key[i] > m) m = key[i];
+    }
+    m = wave_max_u64(m);
+    if (lane == g) gkey = m;
+  }
+  uint64_t kept = 0;  // bit g: group g kept (n_group <= 64)
+  for (int r = 0; r < topk_group; ++r) {
+    const uint64_t best = wave_max_u64(gkey);
+    const int g = (int)(~(uint32_t)best) / gs;
+    kept |= 1ull << g;
+    if (lane == g) gkey = 0;
+  }
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E && !((kept >> (e / gs)) & 1ull)) key[i] = 0ull;
+  }
+}
+
+// Routing options (Dots3NoteTextConfig n_group, topk_group, norm_topk_prob,
+// routed_scaling_factor).
+struct RouteOpts {
+  int n_group, topk_group;
+  bool renormalize;
+  float scaling;
+};
+
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int K,
-                                                    int32_t* __restrict__ ids, float* __restrict__ wts) {
+                                                    RouteOpts opt, int32_t* __restrict__ ids,
+                                                    float* __restrict__ wts) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -179,42 +237,52 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     const int e = lane + 64 * i;
     key[i] = e < E ? route_key(row[e], (uint32_t)e) : 0ull;  // 0 sorts below every finite key
   }
+  if (opt.n_group > 1) keep_best_groups(key, lane, E, opt.n_group, opt.topk_group);
   uint64_t mine = 0;
   for (int k = 0; k < K; ++k) {
     uint64_t best = key[0];
 #pragma unroll
     for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, off);
-      best = o > best ? o : best;
-    }
+    best = wave_max_u64(best);
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
       if (key[i] == best) key[i] = 0ull;
     if (lane == k) mine = best;
   }
-  // Weights: exp(l_k - l_max) / sum over the selected set, in double, rounded once.
+  // Weights: exp(l_k - l_max) over the selected set (renormalised) or over all
+  // E experts, in double, times the scaling factor, rounded once. Slot 0 holds
+  // the largest logit of all experts (its group always has the best score).
   const float v = key_value(mine);
   const float vmax = __shfl(v, 0);
-  double ex = lane < K ? exp((double)v - (double)vmax) : 0.0;
-  double sum = ex;
+  const double ex = lane < K ? exp((double)v - (double)vmax) : 0.0;
+  double sum;
+  if (opt.renormalize) {
+    sum = wave_sum_f64(ex);
+  } else {
+    double part = 0.0;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sum += shfl_xor_f64(sum, off);
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) part += exp((double)row[e] - (double)vmax);
+    }
+    sum = wave_sum_f64(part);
+  }
   if (lane < K) {
     ids[(int64_t)t * K + lane] = (int32_t)(~(uint32_t)mine);
-    wts[(int64_t)t * K + lane] = (float)(ex / sum);
+    wts[(int64_t)t * K + lane] = (float)(ex / sum * (double)opt.scaling);
   }
 }
 
-hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w, hipStream_t stream) {
+hipError_t launch_route(const float* logits, int T, int E, int K, int n_group, int topk_group, bool renormalize,
+                        float scaling, int32_t* ids, float* w, hipStream_t stream) {
   const dim3 grid((T + 3) / 4);
   const int vpl = (E + 63) / 64;
-  if (vpl <= 1) route_kernel<1><<<grid, 256, 0, stream>>>(logits, T, E, K, ids, w);
-  else if (vpl <= 2) route_kernel<2><<<grid, 256, 0, stream>>>(logits, T, E, K, ids, w);
-  else if (vpl <= 4) route_kernel<4><<<grid, 256, 0, stream>>>(logits, T, E, K, ids, w);
-  else if (vpl <= 8) route_kernel<8><<<grid, 256, 0, stream>>>(logits, T, E, K, ids, w);
-  else route_kernel<16><<<grid, 256, 0, stream>>>(logits, T, E, K, ids, w);
+  const RouteOpts opt{n_group, topk_group, renormalize, scaling};
+  if (vpl <= 1) route_kernel<1><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
+  else if (vpl <= 2) route_kernel<2><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
+  else if (vpl <= 4) route_kernel<4><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
+  else if (vpl <= 8) route_kernel<8><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
+  else route_kernel<16><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
   return hipGetLastError();
 }
 

@@ -26,10 +26,13 @@ class MoELayer:
     """One MoE layer's experts on this GPU: routed experts [e0, e0+E_loc) and the shared expert."""
 
     def __init__(self, H: int, F: int, F_s: int, E: int, E_loc: int, e0: int, K: int, dtype: str,
-                 device: str | torch.device = "cuda"):
+                 device: str | torch.device = "cuda", n_group: int = 1, topk_group: int = 0,
+                 renormalize: bool = True, routed_scaling_factor: float = 1.0):
         if dtype not in ("bf16", "fp8"):
             raise ValueError("dtype must be 'bf16' or 'fp8'")
         self.H, self.F, self.F_s, self.E, self.E_loc, self.e0, self.K = H, F, F_s, E, E_loc, e0, K
+        self.n_group, self.topk_group = n_group, topk_group
+        self.renormalize, self.routed_scaling_factor = renormalize, routed_scaling_factor
         self.dtype = dtype
         self.code = L.DMOE_FP8_E4M3 if dtype == "fp8" else L.DMOE_BF16
         self.device = torch.device(device)
@@ -94,7 +97,8 @@ class MoELayer:
     # ------------------------------------------------------------------ forward
     def desc(self, T: int, T_s: int, logits_given: bool) -> L.LayerDesc:
         return L.LayerDesc(T, self.H, self.F, self.F_s if T_s > 0 else 0, self.E, self.E_loc, self.e0, self.K,
-                           T_s if self.F_s else 0, self.code, 1 if logits_given else 0)
+                           T_s if self.F_s else 0, self.code, 1 if logits_given else 0, self.n_group,
+                           self.topk_group, 0 if self.renormalize else 1, self.routed_scaling_factor)
 
     def workspace(self, desc: L.LayerDesc) -> torch.Tensor:
         key = tuple(getattr(desc, n) for n, _ in L.LayerDesc._fields_)

@@ -66,7 +66,7 @@ typedef int32_t dmoe_status;
 #define DMOE_BF16 1
 #define DMOE_FP8_E4M3 2
 
-#define DMOE_ABI_VERSION 1
+#define DMOE_ABI_VERSION 2
 
 /* Text of the last error on this thread ("" if none). Host pointer, valid
  * until the next call on the same thread. */
@@ -101,6 +101,27 @@ dmoe_status dmoe_router_logits(const uint16_t* x, int64_t ldx, const float* w_r,
  */
 dmoe_status dmoe_route(const float* logits, int32_t T, int32_t E, int32_t K, int32_t* topk_ids, float* topk_w,
                        hipStream_t stream);
+
+/*
+ * Top-K routing with the other Dots3NoteTextConfig routing knobs (n_group,
+ * topk_group, norm_topk_prob, routed_scaling_factor):
+ * - n_group > 1: the E experts form n_group groups of E / n_group consecutive
+ *   experts; a group's score is its largest logit; the topk_group groups with
+ *   the largest scores are kept (equal scores: the lower group) and the K
+ *   experts are the top-K (same tie rule) of the kept groups' experts. The
+ *   docs fix only that the selected experts lie within topk_group groups; the
+ *   group's best expert as its score is this library's reading.
+ * - renormalize != 0: weights as dmoe_route; 0: the softmax over all E experts
+ *   of each selected expert, not renormalised.
+ * - weights are multiplied by routed_scaling_factor before the FP32 rounding.
+ * n_group 0 or 1: ungrouped; topk_group 0: every group. Requires n_group <= 64,
+ * E % n_group == 0, 1 <= topk_group <= n_group, K <= topk_group * E / n_group,
+ * and a positive finite routed_scaling_factor; otherwise as dmoe_route.
+ * dmoe_route(...) is dmoe_route_grouped(..., 1, 1, 1, 1.0f, ...).
+ */
+dmoe_status dmoe_route_grouped(const float* logits, int32_t T, int32_t E, int32_t K, int32_t n_group,
+                               int32_t topk_group, int32_t renormalize, float routed_scaling_factor,
+                               int32_t* topk_ids, float* topk_w, hipStream_t stream);
 
 /*
  * Expert-contiguous permutation of the (token, slot) pairs routed to this
@@ -220,6 +241,11 @@ typedef struct dmoe_layer_desc {
   int32_t T_s;          /* the shared expert runs on tokens [0, T_s) */
   int32_t dtype;        /* DMOE_BF16 or DMOE_FP8_E4M3 */
   int32_t logits_given; /* 1: ptrs.logits is an input; 0: computed from x and w_router */
+  /* Routing options as in dmoe_route_grouped; zero values select the defaults. */
+  int32_t n_group;              /* 0 or 1: ungrouped */
+  int32_t topk_group;           /* 0: every group */
+  int32_t no_renormalize;       /* 0: renormalise over the selected experts (norm_topk_prob) */
+  float routed_scaling_factor;  /* 0: 1.0 */
 } dmoe_layer_desc;
 
 typedef struct dmoe_layer_ptrs {

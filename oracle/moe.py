@@ -354,7 +354,8 @@ def moe_forward(cfg, x_bits: np.ndarray, weights: Callable, w_r: np.ndarray | No
                 logits: np.ndarray | None = None, tokens: np.ndarray | None = None) -> OracleResult:
     """Forward of one MoE layer for all tokens, or for the listed ``tokens`` only.
 
-    cfg: object with T, H, F, F_s, E, e0, E_loc, K, T_s, dtype.
+    cfg: object with T, H, F, F_s, E, e0, E_loc, K, T_s, dtype, and optionally the
+    routing options n_group, topk_group (0: every group), renormalize, scaling.
     x_bits: [T, H] bfloat16 bits. weights(which, e) returns expert e's
     "gate"/"up"/"down" weight (float32 for FP8, bfloat16 bits for BF16; e = -1
     is the shared expert). Either w_r (router weight, float32 [E, H]) or given
@@ -367,7 +368,8 @@ def moe_forward(cfg, x_bits: np.ndarray, weights: Callable, w_r: np.ndarray | No
     tok = np.arange(cfg.T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     x = bf16_to_f64(np.asarray(x_bits)[tok])
     L = router_logits(x, w_r) if logits is None else np.asarray(logits, dtype=np.float32)[tok]
-    ids, w = route(L, cfg.K)
+    ids, w = route(L, cfg.K, n_group=getattr(cfg, "n_group", 1), topk_group=getattr(cfg, "topk_group", 0) or None,
+                   renormalize=getattr(cfg, "renormalize", True), scaling=getattr(cfg, "scaling", 1.0))
     offsets, row_token, _, token_row = permute(ids, cfg.e0, cfg.E_loc)
     if fp8:
         xq, xs = quantize_act(x)

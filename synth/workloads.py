@@ -65,6 +65,11 @@ class LayerConfig:
     T_s: int
     logits: str
     seed: int = 0
+    # routing options (Dots3NoteTextConfig n_group, topk_group, norm_topk_prob, routed_scaling_factor)
+    n_group: int = 1
+    topk_group: int = 0  # 0: every group
+    renormalize: bool = True
+    scaling: float = 1.0
 
     def replace(self, **kw) -> "LayerConfig":
         return dataclasses.replace(self, **kw)

@@ -50,7 +50,8 @@ def weights_provider(cfg):
 def build_layer(cfg, threads=None):
     """MoELayer with every local expert and the shared expert set from the generator."""
     from fp8_expert_ffn_amd import MoELayer
-    layer = MoELayer(cfg.H, cfg.F, cfg.F_s, cfg.E, cfg.E_loc, cfg.e0, cfg.K, cfg.dtype, DEV)
+    layer = MoELayer(cfg.H, cfg.F, cfg.F_s, cfg.E, cfg.E_loc, cfg.e0, cfg.K, cfg.dtype, DEV, n_group=cfg.n_group,
+                     topk_group=cfg.topk_group, renormalize=cfg.renormalize, routed_scaling_factor=cfg.scaling)
     as_bf16 = cfg.dtype == "bf16"
     for which in ("gate", "up", "down"):
         synth.fill_expert_weights(cfg, which, cfg.experts,

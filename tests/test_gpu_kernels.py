@@ -48,6 +48,23 @@ def test_route_full_size_given_logits(ci):
     _route_case(synth.given_logits(cfg), cfg.K)
 
 
+@pytest.mark.parametrize("E,K,G,TG,renorm,scale", [(256, 8, 8, 4, True, 1.0), (256, 8, 8, 4, False, 2.5),
+                                                     (64, 6, 16, 3, True, 1.0), (64, 4, 64, 6, False, 1.0),
+                                                     (1024, 16, 32, 5, True, 0.75), (96, 8, 4, 1, True, 1.0),
+                                                     (256, 8, 1, 1, False, 1.0)])
+def test_route_grouped(E, K, G, TG, renorm, scale):
+    say(f"route grouped E={E} K={K} n_group={G} topk_group={TG} renormalize={renorm} scaling={scale}")
+    rng = np.random.default_rng(E + 7 * G + TG)
+    L = (rng.standard_normal((257, E)) * 1.43).astype(np.float32)
+    L[0] = 0.0                                               # all equal: lower groups, lower experts
+    L[1] = np.repeat(rng.standard_normal(E // 8), 8)[:E]     # equal values inside groups of 8
+    L[2] = np.round(rng.standard_normal(E) * 2)              # integer ties across groups
+    ids, w = dm.dmoe_route_grouped(torch.from_numpy(L).to(DEV), K, G, TG, renorm, scale)
+    ids_r, w_r = oracle.route(L, K, n_group=G, topk_group=TG, renormalize=renorm, scaling=scale)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_r)
+    assert np.max(np.abs(w.cpu().numpy().astype(np.float64) - w_r) / scale) <= W_TOL
+
+
 def test_route_single_token():
     _route_case(np.array([[0.5, 2.0, -1.0, 2.0]], np.float32), 2)
 

@@ -29,6 +29,10 @@ CASES = {
                                            dtype="bf16", T_s=50, logits="uniform"),
     "single_token_fp8": synth.LayerConfig("one_tok", T=1, H=512, F=128, F_s=128, E=16, E_loc=16, e0=0, K=4,
                                           dtype="fp8", T_s=1, logits="router"),
+    # group-limited routing without renormalisation, scaled weights
+    "grouped_fp8": synth.LayerConfig("grouped", T=300, H=512, F=256, F_s=256, E=64, E_loc=64, e0=0, K=8,
+                                     dtype="fp8", T_s=300, logits="router", n_group=8, topk_group=3,
+                                     renormalize=False, scaling=2.5),
     # vision-tower MoE shape (hidden 1536, FFN 2112 = 16.5 blocks, 64 experts, no shared expert)
     "vision_small_bf16": synth.LayerConfig("vision_small", T=256, H=1536, F=2112, F_s=0, E=64, E_loc=64, e0=0,
                                            K=8, dtype="bf16", T_s=0, logits="router"),

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(L):
     for n in _declared():
         assert hasattr(lib, n), f"{n} declared in dmoe.h but not exported"
     assert set(_declared()) <= set(L._lib.EXPORTS) | {"dmoe_last_error", "dmoe_abi_version"}
-    assert lib.dmoe_abi_version() == 1
+    assert lib.dmoe_abi_version() == 2
 
 
 def _status(fn, *args):
@@ -104,3 +104,16 @@ def test_combine_rejects_bad_slot_count_and_width(L):
     assert b"K = 65" in lib.dmoe_last_error()
     assert lib.dmoe_combine(f, 5120, f, f, None, 0, 0, 64, 8, 5124, f, 5124, None) == L._lib.DMOE_ERR_INVALID_ARG
     assert lib.dmoe_combine(None, 5120, None, None, None, 0, 0, 0, 8, 5120, None, 5120, None) == 0  # T == 0
+
+
+def test_route_grouped_rejects_bad_groups(L):
+    lib = L.lib()
+    f = 0x1000
+    bad = L._lib.DMOE_ERR_INVALID_ARG
+    assert lib.dmoe_route_grouped(f, 4, 256, 8, 3, 1, 1, 1.0, f, f, None) == bad    # 256 % 3 != 0
+    assert b"n_group = 3" in lib.dmoe_last_error()
+    assert lib.dmoe_route_grouped(f, 4, 256, 8, 8, 9, 1, 1.0, f, f, None) == bad    # topk_group > n_group
+    assert lib.dmoe_route_grouped(f, 4, 64, 8, 16, 1, 1, 1.0, f, f, None) == bad    # K=8 > 1 group of 4 experts
+    assert lib.dmoe_route_grouped(f, 4, 64, 8, 8, 4, 1, -1.0, f, f, None) == bad    # scaling must be positive
+    assert lib.dmoe_route_grouped(f, 4, 64, 8, 128, 4, 1, 1.0, f, f, None) == bad   # n_group > 64
+    assert lib.dmoe_route_grouped(None, 0, 64, 8, 8, 4, 0, 2.5, None, None, None) == 0  # T == 0
