@@ -204,9 +204,12 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=1, help="workload index (0 tiny, 1 decode, 2 prefill, "
                                                                 "3 EP share, 4 non-divisible, 5 vision BF16, "
-                                                                "6 vision FP8, 7 dense FFN FP8)")
+                                                                "6 vision FP8, 7 dense FFN FP8, "
+                                                                "8/9 speculative verify batch BF16/FP8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the layer captured once in a HIP graph and replayed (decode-style serving)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -287,6 +290,32 @@ def main() -> int:
                 for s, name in enumerate(dm.STAGE_NAMES)}
     log("[bench] stages (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
 
+    graph_rec = None
+    if args.graph:
+        # One dmoe_forward captured on a side stream, then replayed K times on the current stream.
+        y_eager = out["y"].clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                dm.dmoe_forward(d, p, ws)
+        stream.wait_stream(side)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / args.steps
+        same = bool(torch.equal(out["y"].view(torch.int16), y_eager.view(torch.int16)))
+        graph_rec = {"ms_per_step": round(gms, 5), "value": round(cfg.T / (gms / 1e3), 1), "unit": "tokens/s",
+                     "replays": args.steps, "output_identical_to_eager": same}
+        log(f"[bench] graph replay: {gms:.4f} ms/step (eager {ms_step:.4f}); output identical: {same}")
+
     offsets = layer.ws_view(d, ws, "offsets").cpu().numpy()
     acc = accounting(cfg, offsets, cfg.logits == "router")
     sec = ms_step / 1e3
@@ -340,6 +369,8 @@ def main() -> int:
         "stages_note": "separate pass with an event at every stage boundary (markers add a few us each)",
         "roofline": roof,
     }
+    if graph_rec is not None:
+        result["graph"] = graph_rec
     if not args.no_cpu_baseline:
         result["cpu_baseline"], results = cpu_baseline(cfg, x_bits, wr, given, args.cpu_seconds)
         y_gpu = out["y"].view(torch.int16).cpu().numpy().view(np.uint16)

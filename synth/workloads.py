@@ -101,6 +101,12 @@ CONFIGS = [
     # every token's single routing weight is exactly 1, so y is the dense SwiGLU FFN output.
     LayerConfig("dense_fp8", T=4096, H=5120, F=13824, F_s=0, E=1, E_loc=1, e0=0, K=1,
                 dtype="fp8", T_s=0, logits="single"),
+    # Speculative-decoding verify batch: the SGLang cookbook's decode graphs cover batches of up to 32 and NEXTN
+    # verifies 4 draft tokens per step, so one verify step carries 32 x 4 = 128 tokens (both checkpoints).
+    LayerConfig("verify_bf16", T=128, H=5120, F=1536, F_s=1536, E=256, E_loc=256, e0=0, K=8,
+                dtype="bf16", T_s=128, logits="router"),
+    LayerConfig("verify_fp8", T=128, H=5120, F=1536, F_s=1536, E=256, E_loc=256, e0=0, K=8,
+                dtype="fp8", T_s=128, logits="router"),
 ]
 
 
