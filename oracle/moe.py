@@ -57,7 +57,7 @@ import numpy as np
 __all__ = [
     "E4M3_MAX", "e4m3_values", "e4m3_encode", "bf16_to_f64", "bf16_round",
     "quantize_act", "quantize_weight_blocks", "dequantize_act", "dequantize_weight_blocks",
-    "router_logits", "route", "permute", "swiglu_expert", "combine",
+    "router_logits", "route", "sigmoid_scores", "route_sigmoid", "permute", "swiglu_expert", "combine",
     "OracleResult", "moe_forward", "moe_forward_loops",
 ]
 
@@ -257,6 +257,47 @@ def route(logits: np.ndarray, k: int, n_group: int = 1, topk_group: int | None =
     return ids, w.astype(np.float32)
 
 
+def sigmoid_scores(logits: np.ndarray) -> np.ndarray:
+    """Per-expert scores 1 / (1 + exp(-l)), computed in float64 and rounded once to float32."""
+    L = np.asarray(logits, dtype=np.float64)
+    return (1.0 / (1.0 + np.exp(-L))).astype(np.float32)
+
+
+def route_sigmoid(logits: np.ndarray, k: int, bias: np.ndarray | None = None, n_group: int = 1,
+                  topk_group: int | None = None, renormalize: bool = True,
+                  scaling: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
+    """Sigmoid scoring with a selection-only correction bias, as in the routers the Transformers docs ("Dots3Note",
+    model outputs, ``aux_loss`` entry) describe as balancing their experts with a router bias (DeepSeek-V3 and
+    its derivatives); written from that published rule.
+
+    s = sigmoid_scores(L) (FP32); b = f32(s + bias) is used for selection only. With n_group > 1 a group's score
+    is f32(b1 + b2), its two largest b (the one b for a group of one expert), the topk_group best groups are kept
+    (equal scores: the lower group) and the top-k of their experts by b (equal: lower expert) are selected.
+    Weights: the unbiased s of the selected experts, divided by their sum when ``renormalize``, times
+    ``scaling``, computed in float64 and stored as float32. parity pinned (brute force, hand example).
+    """
+    s = sigmoid_scores(logits)
+    T, E = s.shape
+    b = s if bias is None else (s + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+    b = np.where(b == 0, np.float32(0.0), b)
+    topk_group = n_group if topk_group is None else topk_group
+    sel = b.astype(np.float64)
+    if n_group > 1:
+        gs = E // n_group
+        assert E % n_group == 0 and 1 <= topk_group <= n_group and k <= topk_group * gs
+        grouped = np.sort(b.reshape(T, n_group, gs), axis=2)[:, :, ::-1]
+        gscore = grouped[:, :, 0] if gs == 1 else (grouped[:, :, 0] + grouped[:, :, 1]).astype(np.float32)
+        gkeep = np.argsort(-gscore.astype(np.float64), axis=1, kind="stable")[:, :topk_group]
+        allowed = np.zeros((T, n_group), dtype=bool)
+        np.put_along_axis(allowed, gkeep, True, axis=1)
+        sel = np.where(np.repeat(allowed, gs, axis=1), sel, -np.inf)
+    ids = np.argsort(-sel, axis=1, kind="stable")[:, :k].astype(np.int32)
+    w = np.take_along_axis(s.astype(np.float64), ids.astype(np.int64), axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return ids, (w * float(scaling)).astype(np.float32)
+
+
 def permute(ids: np.ndarray, e0: int, e_loc: int):
     """Group the (token, slot) pairs whose expert is local into expert-contiguous rows.
 
@@ -351,11 +392,14 @@ def _expert_weights(cfg, weights: Callable, e: int, fp8: bool):
 
 
 def moe_forward(cfg, x_bits: np.ndarray, weights: Callable, w_r: np.ndarray | None = None,
-                logits: np.ndarray | None = None, tokens: np.ndarray | None = None) -> OracleResult:
+                logits: np.ndarray | None = None, tokens: np.ndarray | None = None,
+                score_bias: np.ndarray | None = None) -> OracleResult:
     """Forward of one MoE layer for all tokens, or for the listed ``tokens`` only.
 
     cfg: object with T, H, F, F_s, E, e0, E_loc, K, T_s, dtype, and optionally the
-    routing options n_group, topk_group (0: every group), renormalize, scaling.
+    routing options n_group, topk_group (0: every group), renormalize, scaling and
+    scoring ("softmax" or "sigmoid", the latter with the optional per-expert
+    selection bias ``score_bias``).
     x_bits: [T, H] bfloat16 bits. weights(which, e) returns expert e's
     "gate"/"up"/"down" weight (float32 for FP8, bfloat16 bits for BF16; e = -1
     is the shared expert). Either w_r (router weight, float32 [E, H]) or given
@@ -368,8 +412,12 @@ def moe_forward(cfg, x_bits: np.ndarray, weights: Callable, w_r: np.ndarray | No
     tok = np.arange(cfg.T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     x = bf16_to_f64(np.asarray(x_bits)[tok])
     L = router_logits(x, w_r) if logits is None else np.asarray(logits, dtype=np.float32)[tok]
-    ids, w = route(L, cfg.K, n_group=getattr(cfg, "n_group", 1), topk_group=getattr(cfg, "topk_group", 0) or None,
-                   renormalize=getattr(cfg, "renormalize", True), scaling=getattr(cfg, "scaling", 1.0))
+    ropts = dict(n_group=getattr(cfg, "n_group", 1), topk_group=getattr(cfg, "topk_group", 0) or None,
+                 renormalize=getattr(cfg, "renormalize", True), scaling=getattr(cfg, "scaling", 1.0))
+    if getattr(cfg, "scoring", "softmax") == "sigmoid":
+        ids, w = route_sigmoid(L, cfg.K, bias=score_bias, **ropts)
+    else:
+        ids, w = route(L, cfg.K, **ropts)
     offsets, row_token, _, token_row = permute(ids, cfg.e0, cfg.E_loc)
     if fp8:
         xq, xs = quantize_act(x)

@@ -214,3 +214,67 @@ def test_grouped_route_degenerate_cases_reduce_to_ungrouped():
     # one expert per group: group selection is itself a top-topk_group, then top-k of those
     ids, _ = oracle.route(L, 4, n_group=64, topk_group=6)
     np.testing.assert_array_equal(ids, base[0][:, :4])
+
+
+def _brute_sigmoid(lrow, bias, k, n_group, topk_group):
+    """Every rank counted explicitly: scores in float64 rounded to float32, biased scores for selection, groups
+    scored by their two best biased scores."""
+    s = np.array([np.float32(1.0 / (1.0 + np.exp(-float(v)))) for v in lrow], np.float32)
+    b = np.array([np.float32(s[e] + np.float32(bias[e])) for e in range(lrow.size)], np.float32)
+    E = lrow.size
+    gs = E // n_group
+    if gs == 1:
+        score = [float(b[g]) for g in range(n_group)]
+    else:
+        score = []
+        for g in range(n_group):
+            top = sorted((float(v) for v in b[g * gs:(g + 1) * gs]), reverse=True)
+            score.append(float(np.float32(np.float32(top[0]) + np.float32(top[1]))))
+    keep = [g for g in range(n_group)
+            if sum((score[h] > score[g]) or (score[h] == score[g] and h < g) for h in range(n_group)) < topk_group]
+    allowed = [e for e in range(E) if e // gs in keep]
+    out = [None] * k
+    for e in allowed:
+        r = sum((b[f] > b[e]) or (b[f] == b[e] and f < e) for f in allowed)
+        if r < k:
+            out[r] = e
+    return np.array(out), s
+
+
+def test_sigmoid_route_hand_example():
+    # logits 0 -> s = 0.5 exactly; bias moves expert 3 ahead of expert 1 for selection only
+    L = np.array([[2.0, 1.0, 0.0, 0.5]], np.float32)
+    bias = np.array([0.0, 0.0, 0.0, 0.2], np.float32)
+    ids, w = oracle.route_sigmoid(L, 2, bias=bias)
+    s = 1.0 / (1.0 + np.exp(-np.array([2.0, 1.0, 0.0, 0.5])))
+    assert s[3] + 0.2 > s[1]
+    np.testing.assert_array_equal(ids, [[0, 3]])
+    np.testing.assert_allclose(w[0], s[[0, 3]] / s[[0, 3]].sum(), rtol=1e-7)   # unbiased scores, renormalised
+    ids2, w2 = oracle.route_sigmoid(L, 2, bias=bias, renormalize=False, scaling=2.0)
+    np.testing.assert_allclose(w2[0], 2.0 * s[[0, 3]], rtol=1e-6)
+
+
+@pytest.mark.parametrize("E,K,G,TG", [(8, 3, 1, 1), (16, 4, 4, 2), (12, 5, 3, 2), (64, 8, 8, 4), (32, 4, 32, 5)])
+def test_sigmoid_route_matches_brute_force(E, K, G, TG):
+    rng = np.random.default_rng(E * 17 + G)
+    L = np.concatenate([_adversarial_logits(E, rng), (rng.standard_normal((30, E)) * 2).astype(np.float32)])
+    bias = (rng.standard_normal(E) * 0.05).astype(np.float32)
+    bias[: E // 4] = 0.0
+    ids, w = oracle.route_sigmoid(L, K, bias=bias, n_group=G, topk_group=TG)
+    for t in range(L.shape[0]):
+        ref, s = _brute_sigmoid(L[t], bias, K, G, TG)
+        np.testing.assert_array_equal(ids[t], ref)
+        sel = s[ref].astype(np.float64)
+        np.testing.assert_allclose(w[t], sel / sel.sum(), rtol=1e-6)
+
+
+def test_sigmoid_route_without_bias_is_monotone_in_logits():
+    """With no bias and no groups, sigmoid is monotone: the selected set equals the softmax router's."""
+    rng = np.random.default_rng(9)
+    L = (rng.standard_normal((200, 64)) * 3).astype(np.float32)
+    ids_s, _ = oracle.route_sigmoid(L, 8)
+    ids_m, _ = oracle.route(L, 8)
+    # equal float32 sigmoid values (saturated logits) may break ties differently; compare where distinct
+    s = oracle.sigmoid_scores(L)
+    distinct = np.array([np.unique(np.sort(s[t])[::-1][:9]).size == 9 for t in range(L.shape[0])])
+    np.testing.assert_array_equal(ids_s[distinct], ids_m[distinct])
