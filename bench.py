@@ -39,7 +39,10 @@ def build_layer(cfg, dev):
     import synth
     from fp8_expert_ffn_amd import MoELayer
     layer = MoELayer(cfg.H, cfg.F, cfg.F_s, cfg.E, cfg.E_loc, cfg.e0, cfg.K, cfg.dtype, dev, n_group=cfg.n_group,
-                     topk_group=cfg.topk_group, renormalize=cfg.renormalize, routed_scaling_factor=cfg.scaling)
+                     topk_group=cfg.topk_group, renormalize=cfg.renormalize, routed_scaling_factor=cfg.scaling,
+                     scoring=cfg.scoring)
+    if cfg.scoring == "sigmoid":
+        layer.set_score_bias(synth.score_bias(cfg))
     bf16 = cfg.dtype == "bf16"
     for which in ("gate", "up", "down"):
         synth.fill_expert_weights(cfg, which, cfg.experts, lambda i, a, w=which: layer.set_weight(w, i, a), bf16)
@@ -153,7 +156,8 @@ def cpu_baseline(cfg, x_bits, wr, given, seconds: float):
     results = []
     while True:
         tok = np.sort(rng.choice(cfg.T, size=min(n, cfg.T), replace=False))
-        results.append(oracle.moe_forward(cfg, x_bits, get, w_r=wr, logits=given, tokens=tok))
+        results.append(oracle.moe_forward(cfg, x_bits, get, w_r=wr, logits=given, tokens=tok,
+                                          score_bias=synth.score_bias(cfg) if cfg.scoring == "sigmoid" else None))
         done += tok.size
         el = time.perf_counter() - t0
         if el >= seconds or done >= cfg.T:

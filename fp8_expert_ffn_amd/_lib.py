@@ -23,9 +23,12 @@ DMOE_ERR_WORKSPACE = 4
 DMOE_ERR_HIP = 5
 DMOE_BF16 = 1
 DMOE_FP8_E4M3 = 2
+DMOE_SCORING_SOFTMAX = 0
+DMOE_SCORING_SIGMOID = 1
 
 EXPORTS = [
     "dmoe_last_error", "dmoe_abi_version", "dmoe_router_logits", "dmoe_route", "dmoe_route_grouped",
+    "dmoe_route_sigmoid",
     "dmoe_permute_ws_bytes",
     "dmoe_permute", "dmoe_quant_act", "dmoe_quant_weight_blocks", "dmoe_gemm_ws_bytes",
     "dmoe_grouped_gemm_gateup", "dmoe_grouped_gemm_down", "dmoe_shared_expert_ws_bytes", "dmoe_shared_expert",
@@ -44,13 +47,14 @@ class DmoeError(RuntimeError):
 class LayerDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "H", "F", "F_s", "E", "E_loc", "e0", "K", "T_s", "dtype", "logits_given",
-                 "n_group", "topk_group", "no_renormalize")] + [("routed_scaling_factor", ctypes.c_float)]
+                 "n_group", "topk_group", "no_renormalize")] + [("routed_scaling_factor", ctypes.c_float),
+                                                                 ("scoring", ctypes.c_int32)]
 
 
 class LayerPtrs(ctypes.Structure):
     _fields_ = [
         ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64),
-        ("w_router", ctypes.c_void_p), ("logits", ctypes.c_void_p),
+        ("w_router", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("score_bias", ctypes.c_void_p),
         ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
         ("ldw_gu", ctypes.c_int64), ("ldw_d", ctypes.c_int64),
         ("ws_gate", ctypes.c_void_p), ("ws_up", ctypes.c_void_p), ("ws_down", ctypes.c_void_p),
@@ -71,6 +75,7 @@ _SIGS = {
     "dmoe_router_logits": ([P, I64, P, I32, I32, I32, P, P], I32),
     "dmoe_route": ([P, I32, I32, I32, P, P, P], I32),
     "dmoe_route_grouped": ([P, I32, I32, I32, I32, I32, I32, ctypes.c_float, P, P, P], I32),
+    "dmoe_route_sigmoid": ([P, P, I32, I32, I32, I32, I32, I32, ctypes.c_float, P, P, P], I32),
     "dmoe_permute_ws_bytes": ([I32, I32, I32], SZ),
     "dmoe_permute": ([P, I32, I32, I32, I32, P, P, P, P, P, SZ, P], I32),
     "dmoe_quant_act": ([P, I32, I32, I64, P, I64, P, I64, P], I32),
@@ -148,6 +153,20 @@ def dmoe_route(logits: torch.Tensor, K: int, topk_ids=None, topk_w=None, stream=
     if topk_w is None:
         topk_w = torch.empty((T, K), dtype=torch.float32, device=logits.device)
     _check(lib().dmoe_route(ptr(logits), T, E, K, ptr(topk_ids), ptr(topk_w), stream_handle(stream)))
+    return topk_ids, topk_w
+
+
+def dmoe_route_sigmoid(logits: torch.Tensor, K: int, score_bias: torch.Tensor | None = None, n_group: int = 1,
+                       topk_group: int = 0, renormalize: bool = True, routed_scaling_factor: float = 1.0,
+                       topk_ids=None, topk_w=None, stream=None):
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, K), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, K), dtype=torch.float32, device=logits.device)
+    _check(lib().dmoe_route_sigmoid(ptr(logits), ptr(score_bias) if score_bias is not None else None, T, E, K,
+                                    n_group, topk_group, 1 if renormalize else 0, routed_scaling_factor,
+                                    ptr(topk_ids), ptr(topk_w), stream_handle(stream)))
     return topk_ids, topk_w
 
 

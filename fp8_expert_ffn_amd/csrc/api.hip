@@ -125,6 +125,23 @@ dmoe_status dmoe_route(const float* logits, int32_t T, int32_t E, int32_t K, int
   return dmoe_route_grouped(logits, T, E, K, 1, 1, 1, 1.0f, topk_ids, topk_w, stream);
 }
 
+dmoe_status dmoe_route_sigmoid(const float* logits, const float* score_bias, int32_t T, int32_t E, int32_t K,
+                               int32_t n_group, int32_t topk_group, int32_t renormalize, float routed_scaling_factor,
+                               int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  REQ(T >= 0, DMOE_ERR_INVALID_ARG, "T = %d < 0", T);
+  REQ(E >= 1 && E <= 1024, DMOE_ERR_INVALID_ARG, "E = %d outside [1, 1024]", E);
+  REQ(K >= 1 && K <= E && K <= 64, DMOE_ERR_INVALID_ARG, "K = %d outside [1, min(E, 64)]", K);
+  TRY(check_route_opts(E, K, n_group, topk_group, routed_scaling_factor));
+  if (T == 0) return ok();
+  REQ_PTR(logits, "logits");
+  REQ_PTR(topk_ids, "topk_ids");
+  REQ_PTR(topk_w, "topk_w");
+  const int g = n_group <= 1 ? 1 : n_group;
+  return hip_status(launch_route_sigmoid(logits, score_bias, T, E, K, g, topk_group <= 0 ? g : topk_group,
+                                         renormalize != 0, routed_scaling_factor, topk_ids, topk_w, stream),
+                    "route launch");
+}
+
 size_t dmoe_permute_ws_bytes(int32_t T, int32_t K, int32_t E_loc) {
   if (T < 0 || K < 1 || E_loc < 1) return 0;
   return permute_ws_bytes(T, K, E_loc);
@@ -439,6 +456,8 @@ dmoe_status check_desc(const dmoe_layer_desc* d) {
   REQ((int64_t)d->T * d->K <= INT32_MAX / 2, DMOE_ERR_INVALID_ARG, "T*K too large");
   TRY(check_route_opts(d->E, d->K, d->n_group, d->topk_group,
                        d->routed_scaling_factor == 0.f ? 1.f : d->routed_scaling_factor));
+  REQ(d->scoring == DMOE_SCORING_SOFTMAX || d->scoring == DMOE_SCORING_SIGMOID, DMOE_ERR_INVALID_ARG,
+      "scoring = %d is not DMOE_SCORING_SOFTMAX or DMOE_SCORING_SIGMOID", d->scoring);
   return DMOE_OK;
 }
 }  // namespace
@@ -520,10 +539,16 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
   STEP(mark(), "event");
   {
     const int g = d->n_group <= 1 ? 1 : d->n_group;
-    STEP(launch_route(p->logits, d->T, d->E, d->K, g, d->topk_group <= 0 ? g : d->topk_group,
-                      d->no_renormalize == 0, d->routed_scaling_factor == 0.f ? 1.f : d->routed_scaling_factor,
-                      p->topk_ids, p->topk_w, stream),
-         "route");
+    const int tg = d->topk_group <= 0 ? g : d->topk_group;
+    const float sc = d->routed_scaling_factor == 0.f ? 1.f : d->routed_scaling_factor;
+    if (d->scoring == DMOE_SCORING_SIGMOID)
+      STEP(launch_route_sigmoid(p->logits, p->score_bias, d->T, d->E, d->K, g, tg, d->no_renormalize == 0, sc,
+                                p->topk_ids, p->topk_w, stream),
+           "route");
+    else
+      STEP(launch_route(p->logits, d->T, d->E, d->K, g, tg, d->no_renormalize == 0, sc, p->topk_ids, p->topk_w,
+                        stream),
+           "route");
   }
   STEP(mark(), "event");
   STEP(launch_permute(p->topk_ids, d->T, d->K, d->e0, d->E_loc, offsets, row_token, row_slot, token_row,

@@ -20,6 +20,10 @@ hipError_t launch_router_logits(const uint16_t* x, int64_t ldx, const float* w_r
 // n_group <= 1: ungrouped; renormalize: divide by the selected experts' sum (norm_topk_prob)
 hipError_t launch_route(const float* logits, int T, int E, int K, int n_group, int topk_group, bool renormalize,
                         float scaling, int32_t* ids, float* w, hipStream_t stream);
+// sigmoid scoring; bias: per-expert selection bias or nullptr
+hipError_t launch_route_sigmoid(const float* logits, const float* bias, int T, int E, int K, int n_group,
+                                int topk_group, bool renormalize, float scaling, int32_t* ids, float* w,
+                                hipStream_t stream);
 
 // permute.hip
 constexpr int kPermutePairs = 512;  // (token, slot) pairs per permutation block

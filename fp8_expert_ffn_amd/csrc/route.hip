@@ -273,6 +273,106 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   }
 }
 
+// ---------------------------------------------------------------------------
+// Sigmoid scoring with a selection-only correction bias (the bias-balanced
+// routers the Transformers docs name in their aux_loss entry: DeepSeek-V3 and
+// its derivatives). s = f32(1 / (1 + exp(-l))) evaluated in double; the key
+// of expert e is f32(s + bias[e]); a group's score is f32(b1 + b2), its two
+// largest biased scores; weights come from the unbiased s.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sigmoid_score(float l) { return (float)(1.0 / (1.0 + exp(-(double)l))); }
+
+template <int VPL>
+__global__ __launch_bounds__(256) void route_sigmoid_kernel(const float* __restrict__ logits,
+                                                            const float* __restrict__ bias, int T, int E, int K,
+                                                            RouteOpts opt, int32_t* __restrict__ ids,
+                                                            float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (int64_t)t * E;
+  uint64_t key[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      const float b = sigmoid_score(row[e]) + (bias ? bias[e] : 0.f);
+      key[i] = route_key(b, (uint32_t)e);
+    } else {
+      key[i] = 0ull;
+    }
+  }
+  if (opt.n_group > 1) {
+    const int gs = E / opt.n_group;
+    uint64_t gkey = 0;  // lane g: key of group g's score
+    for (int g = 0; g < opt.n_group; ++g) {
+      uint64_t m1 = 0;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && e / gs == g && key[i] > m1) m1 = key[i];
+      }
+      m1 = wave_max_u64(m1);
+      float score = key_value(m1);
+      if (gs > 1) {
+        uint64_t m2 = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+          const int e = lane + 64 * i;
+          if (e < E && e / gs == g && key[i] != m1 && key[i] > m2) m2 = key[i];
+        }
+        m2 = wave_max_u64(m2);
+        score = score + key_value(m2);
+      }
+      if (lane == g) gkey = route_key(score, (uint32_t)g);
+    }
+    uint64_t kept = 0;
+    for (int r = 0; r < opt.topk_group; ++r) {
+      const uint64_t best = wave_max_u64(gkey);
+      const int g = (int)(~(uint32_t)best);
+      kept |= 1ull << g;
+      if (lane == g) gkey = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((kept >> (e / gs)) & 1ull)) key[i] = 0ull;
+    }
+  }
+  uint64_t mine = 0;
+  for (int k = 0; k < K; ++k) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (key[i] == best) key[i] = 0ull;
+    if (lane == k) mine = best;
+  }
+  const int e = (int)(~(uint32_t)mine);
+  const double s = lane < K ? (double)sigmoid_score(row[e]) : 0.0;
+  const double sum = opt.renormalize ? wave_sum_f64(s) : 1.0;
+  if (lane < K) {
+    ids[(int64_t)t * K + lane] = e;
+    wts[(int64_t)t * K + lane] = (float)(s / sum * (double)opt.scaling);
+  }
+}
+
+hipError_t launch_route_sigmoid(const float* logits, const float* bias, int T, int E, int K, int n_group,
+                                int topk_group, bool renormalize, float scaling, int32_t* ids, float* w,
+                                hipStream_t stream) {
+  const dim3 grid((T + 3) / 4);
+  const int vpl = (E + 63) / 64;
+  const RouteOpts opt{n_group, topk_group, renormalize, scaling};
+  if (vpl <= 1) route_sigmoid_kernel<1><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
+  else if (vpl <= 2) route_sigmoid_kernel<2><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
+  else if (vpl <= 4) route_sigmoid_kernel<4><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
+  else if (vpl <= 8) route_sigmoid_kernel<8><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
+  else route_sigmoid_kernel<16><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const float* logits, int T, int E, int K, int n_group, int topk_group, bool renormalize,
                         float scaling, int32_t* ids, float* w, hipStream_t stream) {
   const dim3 grid((T + 3) / 4);

@@ -27,12 +27,16 @@ class MoELayer:
 
     def __init__(self, H: int, F: int, F_s: int, E: int, E_loc: int, e0: int, K: int, dtype: str,
                  device: str | torch.device = "cuda", n_group: int = 1, topk_group: int = 0,
-                 renormalize: bool = True, routed_scaling_factor: float = 1.0):
+                 renormalize: bool = True, routed_scaling_factor: float = 1.0, scoring: str = "softmax"):
         if dtype not in ("bf16", "fp8"):
             raise ValueError("dtype must be 'bf16' or 'fp8'")
         self.H, self.F, self.F_s, self.E, self.E_loc, self.e0, self.K = H, F, F_s, E, E_loc, e0, K
         self.n_group, self.topk_group = n_group, topk_group
         self.renormalize, self.routed_scaling_factor = renormalize, routed_scaling_factor
+        if scoring not in ("softmax", "sigmoid"):
+            raise ValueError("scoring must be 'softmax' or 'sigmoid'")
+        self.scoring = scoring
+        self.score_bias = None  # [E] FP32 selection bias (sigmoid scoring), see set_score_bias
         self.dtype = dtype
         self.code = L.DMOE_FP8_E4M3 if dtype == "fp8" else L.DMOE_BF16
         self.device = torch.device(device)
@@ -95,10 +99,18 @@ class MoELayer:
             L.dmoe_quant_weight_blocks(tmp, q=w, scales=s, stream=stream)
 
     # ------------------------------------------------------------------ forward
+    def set_score_bias(self, bias) -> None:
+        """Per-expert FP32 selection bias for sigmoid scoring ([E], host array or tensor)."""
+        b = torch.as_tensor(bias, dtype=torch.float32)
+        if b.shape != (self.E,):
+            raise ValueError(f"score bias must have shape ({self.E},)")
+        self.score_bias = b.to(self.device).contiguous()
+
     def desc(self, T: int, T_s: int, logits_given: bool) -> L.LayerDesc:
         return L.LayerDesc(T, self.H, self.F, self.F_s if T_s > 0 else 0, self.E, self.E_loc, self.e0, self.K,
                            T_s if self.F_s else 0, self.code, 1 if logits_given else 0, self.n_group,
-                           self.topk_group, 0 if self.renormalize else 1, self.routed_scaling_factor)
+                           self.topk_group, 0 if self.renormalize else 1, self.routed_scaling_factor,
+                           L.DMOE_SCORING_SIGMOID if self.scoring == "sigmoid" else L.DMOE_SCORING_SOFTMAX)
 
     def workspace(self, desc: L.LayerDesc) -> torch.Tensor:
         key = tuple(getattr(desc, n) for n, _ in L.LayerDesc._fields_)
@@ -129,6 +141,7 @@ class MoELayer:
         p.x, p.ldx = L.ptr(x), x.stride(0)
         p.w_router = L.ptr(w_router) if not given else None
         p.logits = L.ptr(logits)
+        p.score_bias = L.ptr(self.score_bias) if self.score_bias is not None else None
         p.w_gate, p.w_up, p.w_down = L.ptr(self.w_gate), L.ptr(self.w_up), L.ptr(self.w_down)
         p.ldw_gu, p.ldw_d = self.H, self.fpad
         if self.dtype == "fp8":

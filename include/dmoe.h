@@ -68,6 +68,10 @@ typedef int32_t dmoe_status;
 
 #define DMOE_ABI_VERSION 2
 
+/* Router scoring functions (dmoe_layer_desc.scoring). */
+#define DMOE_SCORING_SOFTMAX 0
+#define DMOE_SCORING_SIGMOID 1
+
 /* Text of the last error on this thread ("" if none). Host pointer, valid
  * until the next call on the same thread. */
 const char* dmoe_last_error(void);
@@ -121,6 +125,22 @@ dmoe_status dmoe_route(const float* logits, int32_t T, int32_t E, int32_t K, int
  */
 dmoe_status dmoe_route_grouped(const float* logits, int32_t T, int32_t E, int32_t K, int32_t n_group,
                                int32_t topk_group, int32_t renormalize, float routed_scaling_factor,
+                               int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/*
+ * Sigmoid scoring with a selection-only correction bias: the bias-balanced
+ * router the Transformers docs ("Dots3Note", model outputs, aux_loss entry)
+ * name for DeepSeek-V3 and derived models.
+ *   s[e] = f32(1 / (1 + exp(-l[e])))  (evaluated in double, rounded once)
+ *   b[e] = f32(s[e] + score_bias[e])  (score_bias may be NULL: no bias)
+ * Selection as dmoe_route_grouped on b, except that a group's score is
+ * f32(b1 + b2), its two largest b (b1 alone for one-expert groups). Weights
+ * are the unbiased s of the selected experts, divided by their sum when
+ * renormalize != 0, times routed_scaling_factor, rounded to FP32.
+ * score_bias: [E] FP32 device array. Same requirements as dmoe_route_grouped.
+ */
+dmoe_status dmoe_route_sigmoid(const float* logits, const float* score_bias, int32_t T, int32_t E, int32_t K,
+                               int32_t n_group, int32_t topk_group, int32_t renormalize, float routed_scaling_factor,
                                int32_t* topk_ids, float* topk_w, hipStream_t stream);
 
 /*
@@ -246,6 +266,7 @@ typedef struct dmoe_layer_desc {
   int32_t topk_group;           /* 0: every group */
   int32_t no_renormalize;       /* 0: renormalise over the selected experts (norm_topk_prob) */
   float routed_scaling_factor;  /* 0: 1.0 */
+  int32_t scoring;              /* DMOE_SCORING_SOFTMAX (0) or DMOE_SCORING_SIGMOID (ptrs.score_bias) */
 } dmoe_layer_desc;
 
 typedef struct dmoe_layer_ptrs {
@@ -253,6 +274,7 @@ typedef struct dmoe_layer_ptrs {
   int64_t ldx;
   const float* w_router; /* [E, H] FP32 (when logits are computed) */
   float* logits;         /* [T, E] FP32: output, or input when logits_given */
+  const float* score_bias; /* [E] FP32 selection bias for sigmoid scoring, or NULL */
   const void* w_gate;    /* routed experts, layout above */
   const void* w_up;
   const void* w_down;

@@ -18,6 +18,7 @@ regenerated without drawing the others. Draws:
 * skewed logits (EP8 share) -- ``-1.1*ln(e+1) + N(0,1)`` in float64, stored as float32.
 * uniform logits (non-divisible stress) -- U[-4, 4) in float64, stored as float32.
 * single logits (dense layer as one expert) -- zeros.
+* ``bias``     -- N(0, 0.01) in float32, the per-expert selection bias of sigmoid scoring.
 
 BF16 workloads store the weights as bfloat16 (round to nearest even of the
 float32 draw); FP8 workloads keep the float32 draw, which each consumer
@@ -33,13 +34,13 @@ import numpy as np
 
 __all__ = [
     "LayerConfig", "CONFIGS", "SHARED", "config", "rng", "f32_to_bf16_bits", "bf16_bits_to_f32",
-    "x_bf16", "router_weight", "given_logits", "expert_weight_f32", "expert_weight_bf16",
+    "x_bf16", "router_weight", "given_logits", "score_bias", "expert_weight_f32", "expert_weight_bf16",
     "fill_expert_weights", "weight_shape", "gen_threads",
 ]
 
 SHARED = -1  # expert index used for the shared expert's streams
 
-_TAGS = {"x": 1, "router": 2, "logits": 3, "gate": 11, "up": 12, "down": 13}
+_TAGS = {"x": 1, "router": 2, "logits": 3, "bias": 4, "gate": 11, "up": 12, "down": 13}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -70,6 +71,7 @@ class LayerConfig:
     topk_group: int = 0  # 0: every group
     renormalize: bool = True
     scaling: float = 1.0
+    scoring: str = "softmax"  # or "sigmoid" (with a per-expert selection bias, see score_bias)
 
     def replace(self, **kw) -> "LayerConfig":
         return dataclasses.replace(self, **kw)
@@ -164,6 +166,12 @@ def given_logits(cfg: LayerConfig) -> np.ndarray:
     if cfg.logits == "single":
         return np.zeros((cfg.T, cfg.E), dtype=np.float32)
     raise ValueError(f"workload {cfg.name} computes its logits from x")
+
+
+def score_bias(cfg: LayerConfig) -> np.ndarray:
+    """Per-expert FP32 selection bias [E] for sigmoid scoring ~ N(0, 0.01)."""
+    g = rng(cfg.seed, "bias")
+    return (g.standard_normal(cfg.E, dtype=np.float32) * np.float32(0.01)).astype(np.float32)
 
 
 def weight_shape(cfg: LayerConfig, which: str, e: int) -> tuple[int, int]:

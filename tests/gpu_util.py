@@ -51,7 +51,10 @@ def build_layer(cfg, threads=None):
     """MoELayer with every local expert and the shared expert set from the generator."""
     from fp8_expert_ffn_amd import MoELayer
     layer = MoELayer(cfg.H, cfg.F, cfg.F_s, cfg.E, cfg.E_loc, cfg.e0, cfg.K, cfg.dtype, DEV, n_group=cfg.n_group,
-                     topk_group=cfg.topk_group, renormalize=cfg.renormalize, routed_scaling_factor=cfg.scaling)
+                     topk_group=cfg.topk_group, renormalize=cfg.renormalize, routed_scaling_factor=cfg.scaling,
+                     scoring=cfg.scoring)
+    if cfg.scoring == "sigmoid":
+        layer.set_score_bias(synth.score_bias(cfg))
     as_bf16 = cfg.dtype == "bf16"
     for which in ("gate", "up", "down"):
         synth.fill_expert_weights(cfg, which, cfg.experts,
@@ -62,6 +65,11 @@ def build_layer(cfg, threads=None):
             layer.set_weight(which, -1, arr)
     torch.cuda.synchronize()
     return layer
+
+
+def score_bias_of(cfg):
+    """The per-expert selection bias for sigmoid-scored workloads (None otherwise)."""
+    return synth.score_bias(cfg) if cfg.scoring == "sigmoid" else None
 
 
 def layer_inputs(cfg):

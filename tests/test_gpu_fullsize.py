@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 from gpu_util import (DEV, LOGIT_TOL, W_TOL, bf16_values, build_layer, compare_y, layer_inputs, near_tie_tokens, say,
-                      to_dev_bf16, weights_provider)
+                      score_bias_of, to_dev_bf16, weights_provider)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +66,8 @@ def test_full_size_workload(ci):
     # --- sampled tokens against the oracle
     tok = _sample_tokens(cfg, SAMPLES[ci])
     t0 = time.time()
-    ref = oracle.moe_forward(cfg, x_bits, weights_provider(cfg), w_r=wr, logits=given, tokens=tok)
+    ref = oracle.moe_forward(cfg, x_bits, weights_provider(cfg), w_r=wr, logits=given, tokens=tok,
+                             score_bias=score_bias_of(cfg))
     say(f"  oracle on {tok.size} tokens in {time.time() - t0:.1f}s")
     if given is None:
         L = out["logits"].cpu().numpy()[tok]

@@ -65,6 +65,26 @@ def test_route_grouped(E, K, G, TG, renorm, scale):
     assert np.max(np.abs(w.cpu().numpy().astype(np.float64) - w_r) / scale) <= W_TOL
 
 
+@pytest.mark.parametrize("E,K,G,TG,renorm,scale,use_bias", [(256, 8, 8, 4, True, 2.5, True),
+                                                              (256, 8, 1, 1, True, 1.0, True),
+                                                              (64, 6, 16, 3, False, 1.0, True),
+                                                              (64, 4, 64, 6, True, 1.0, False),
+                                                              (1024, 16, 32, 5, True, 0.75, True)])
+def test_route_sigmoid(E, K, G, TG, renorm, scale, use_bias):
+    say(f"route sigmoid E={E} K={K} n_group={G} topk_group={TG} renormalize={renorm} scaling={scale} bias={use_bias}")
+    rng = np.random.default_rng(E + 3 * G + TG)
+    L = (rng.standard_normal((257, E)) * 2).astype(np.float32)
+    L[0] = 0.0                                               # equal scores everywhere
+    L[1] = np.round(rng.standard_normal(E) * 2)              # integer ties
+    L[2, : E // 2] = 40.0                                    # saturated scores (s == 1.0 exactly)
+    bias = (rng.standard_normal(E) * 0.05).astype(np.float32) if use_bias else None
+    ids, w = dm.dmoe_route_sigmoid(torch.from_numpy(L).to(DEV), K,
+                                   torch.from_numpy(bias).to(DEV) if use_bias else None, G, TG, renorm, scale)
+    ids_r, w_r = oracle.route_sigmoid(L, K, bias=bias, n_group=G, topk_group=TG, renormalize=renorm, scaling=scale)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_r)
+    assert np.max(np.abs(w.cpu().numpy().astype(np.float64) - w_r) / scale) <= W_TOL
+
+
 def test_route_single_token():
     _route_case(np.array([[0.5, 2.0, -1.0, 2.0]], np.float32), 2)
 

@@ -9,7 +9,7 @@ import torch
 import oracle
 import synth
 from gpu_util import (DEV, LOGIT_TOL, W_TOL, bf16_values, build_layer, compare_y, layer_inputs, near_tie_tokens, say,
-                      to_dev_bf16, weights_provider)
+                      score_bias_of, to_dev_bf16, weights_provider)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +33,10 @@ CASES = {
     "grouped_fp8": synth.LayerConfig("grouped", T=300, H=512, F=256, F_s=256, E=64, E_loc=64, e0=0, K=8,
                                      dtype="fp8", T_s=300, logits="router", n_group=8, topk_group=3,
                                      renormalize=False, scaling=2.5),
+    # sigmoid scoring with a per-expert selection bias, grouped by two-best sums, renormalised
+    "sigmoid_bias_bf16": synth.LayerConfig("sigmoid", T=200, H=512, F=256, F_s=256, E=64, E_loc=64, e0=0, K=6,
+                                           dtype="bf16", T_s=200, logits="router", n_group=8, topk_group=4,
+                                           scoring="sigmoid", scaling=1.5),
     # vision-tower MoE shape (hidden 1536, FFN 2112 = 16.5 blocks, 64 experts, no shared expert)
     "vision_small_bf16": synth.LayerConfig("vision_small", T=256, H=1536, F=2112, F_s=0, E=64, E_loc=64, e0=0,
                                            K=8, dtype="bf16", T_s=0, logits="router"),
@@ -53,7 +57,7 @@ def _run(name):
     x_bits, wr, given = layer_inputs(cfg)
     x = to_dev_bf16(x_bits)
     get = weights_provider(cfg)
-    ref = oracle.moe_forward(cfg, x_bits, get, w_r=wr, logits=given)
+    ref = oracle.moe_forward(cfg, x_bits, get, w_r=wr, logits=given, score_bias=score_bias_of(cfg))
     return cfg, layer, x, x_bits, wr, given, ref
 
 
