@@ -194,8 +194,10 @@ dmoe_status dmoe_quant_weight_blocks(const float* w, int32_t rows, int32_t cols,
  * product is scaled by a_scale * w_scale and added in FP32.
  * h: [max_rows, ldh] BF16, ldh >= round_up(F, 128); columns [F, round_up(F,
  * 128)) are written as 0. Rows past offsets[E_loc] are not written.
- * max_rows: host-side upper bound on offsets[E_loc] (T*K for routed rows),
- * used only to size the grid. ws: at least dmoe_gemm_ws_bytes(max_rows, E_loc).
+ * max_rows: host-side upper bound on offsets[E_loc] (T*K for routed rows); it
+ * sizes the grid and the tile schedule, so it must not be below the real row
+ * count (rows past the capacity it implies are not computed).
+ * ws: at least dmoe_gemm_ws_bytes(max_rows, E_loc).
  */
 size_t dmoe_gemm_ws_bytes(int32_t max_rows, int32_t E_loc);
 dmoe_status dmoe_grouped_gemm_gateup(int32_t dtype, const void* a, int64_t lda, const float* a_scales,
