@@ -71,12 +71,15 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
 //             (the matrix core's own accumulation precision within a slice).
 constexpr int kModeBF16 = 0, kModeFP8X = 1, kModeFP8 = 2;
 
-// Tile kernel. A workgroup (4 waves) owns kBM = 128 rows of one group and
-// 32 * NT weight rows (gate/up: 16 * NT gate + 16 * NT up rows, i.e. 16 * NT
-// columns of h; down: 32 * NT columns of o). Wave (wm, wn) computes rows
-// [64 wm, 64 wm + 64) x 16 * NT weight rows as 4 x NT MFMA tiles of 16x16
-// (NT = 4 by default: two workgroups fit one CU); a tile with at most 64 rows
-// uses 2 x NT MFMA tiles per wave on rows [32 wm, 32 wm + 32). Operands move global -> LDS
+// Tile kernel. A workgroup (2 x WN waves) owns kBM = 128 rows of one group and
+// 16 * NT * WN weight rows (gate/up: 8 * NT * WN gate + as many up rows, i.e.
+// 8 * NT * WN columns of h; down: 16 * NT * WN columns of o). Wave (wm, wn),
+// wm in {0, 1}, wn in [0, WN), computes 16 * MT rows x 16 * NT weight rows as
+// MT x NT MFMA tiles of 16x16, rows [16 MT wm, 16 MT wm + 16 MT): MT = 4 covers
+// the 128 rows, and the last tile of a group runs with MT = ceil(rows / 32) so
+// that short tiles cost MFMA work in proportion to their rows. WN = 2 (256
+// threads, two workgroups per CU) or WN = 4 (512 threads, one workgroup per CU
+// sharing each A stage over twice the weight rows). Operands move global -> LDS
 // with direct (asynchronous, register-free) loads through an NS-stage ring; a
 // stage is 128 bytes of every A and weight row (one 128-wide FP8 scale slice,
 // or 64 BF16 elements) plus the A rows' activation scales. LDS rows are 128
@@ -107,15 +110,31 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
 #ifndef DMOE_TILE_NT_DOWN
 #define DMOE_TILE_NT_DOWN 4
 #endif
+#ifndef DMOE_TILE_WN_GATEUP
+#define DMOE_TILE_WN_GATEUP 2
+#endif
+#ifndef DMOE_TILE_WN_DOWN
+#define DMOE_TILE_WN_DOWN 2
+#endif
+#ifndef DMOE_TILE_NS_WIDE
+#define DMOE_TILE_NS_WIDE 3
+#endif
+#ifndef DMOE_TILE_MT_FINE
+#define DMOE_TILE_MT_FINE 1
+#endif
 
-template <int MODE, bool GATEUP, int NS, int NT>
-__global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gemm_tile_kernel(const TileArgs p,
-                                                                                              int nNB, int n_valid) {
+template <int MODE, bool GATEUP, int NS, int NT, int WN>
+__global__ __launch_bounds__(128 * WN, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gemm_tile_kernel(
+    const TileArgs p, int nNB, int n_valid) {
   constexpr bool kScaled = MODE != kModeBF16;
-  constexpr int NH = NT / 2;           // gate/up: NH gate subtiles, then NH up subtiles per wave
-  constexpr int kRowsB = 32 * NT;      // weight rows per workgroup
-  constexpr int kRows = kBM + kRowsB;  // A rows, then weight rows
-  constexpr int kInstA = kBM / 32, kInstB = kRowsB / 32;  // direct copies per wave per stage
+  constexpr int kThreads = 128 * WN, kWaves = 2 * WN;
+  constexpr int NH = NT / 2;               // gate/up: NH gate subtiles, then NH up subtiles per wave
+  constexpr int kRowsB = 16 * NT * WN;     // weight rows per workgroup
+  constexpr int kHalfB = kRowsB / 2;       // gate/up: gate rows, then as many up rows
+  constexpr int kRows = kBM + kRowsB;      // A rows, then weight rows
+  constexpr int kInstA = kBM / (8 * kWaves), kInstB = kRowsB / (8 * kWaves);  // direct copies per wave per stage
+  static_assert(kInstA * 8 * kWaves == kBM && kInstB * 8 * kWaves == kRowsB, "copy split");
+  static_assert(!GATEUP || kHalfB <= 128, "gate/up: one weight scale block per workgroup");
   static_assert(NS >= 2 && NS <= 4, "pipeline depth");
   // One LDS variable per stage so that each stage is a distinct object.
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kRows * 128];
@@ -171,29 +190,29 @@ __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gem
   const int wm = wave & 1, wn = wave >> 1;
   const int r16 = lane & 15, g4 = lane >> 4;
   // first h (gate/up) or o (down) column of the workgroup and of this wave
-  const int ncol0 = nb * (GATEUP ? 16 * NT : 32 * NT);
+  const int ncol0 = nb * (GATEUP ? kHalfB : kRowsB);
   const int wcol0 = ncol0 + wn * 16 * (GATEUP ? NH : NT);
   const bool active = GATEUP || wcol0 < n_valid;  // down: waves past N only help with the copies
 
-  // Direct-copy sources: copy i of this wave fills LDS rows 8*(4i+wave) .. +7,
-  // lane -> row 8*(4i+wave) + lane/8, 16-byte position lane%8.
+  // Direct-copy sources: copy i of this wave fills LDS rows 8*(kWaves*i+wave) .. +7,
+  // lane -> row 8*(kWaves*i+wave) + lane/8, 16-byte position lane%8.
   int64_t srcA[kInstA];
   const uint8_t* srcB[kInstB];
 #pragma unroll
   for (int i = 0; i < kInstA; ++i) {
-    const int row = 8 * (4 * i + wave) + (lane >> 3);
+    const int row = 8 * (kWaves * i + wave) + (lane >> 3);
     const int m = m0 + row;
     const int64_t arow = a_row(p, gv, m < m_end ? m : m0);  // rows past the group reuse a valid row
     srcA[i] = arow * p.lda_b + 16 * swz(row, lane & 7);
   }
 #pragma unroll
   for (int i = 0; i < kInstB; ++i) {
-    const int row = 8 * (4 * i + wave) + (lane >> 3);
+    const int row = 8 * (kWaves * i + wave) + (lane >> 3);
     int64_t wrow;
     const uint8_t* base;
     if (GATEUP) {
-      wrow = ncol0 + (row % (16 * NT));
-      base = row < 16 * NT ? gv.w0 : gv.w1;
+      wrow = ncol0 + (row % kHalfB);
+      base = row < kHalfB ? gv.w0 : gv.w1;
     } else {
       wrow = ncol0 + row < n_valid ? ncol0 + row : 0;  // rows past N (inactive waves) reread row 0
       base = gv.w0;
@@ -208,9 +227,10 @@ __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gem
   // Weight block scales staged in LDS before the pipeline starts: gate/up: the
   // 128-row block of the gate and of the up rows; down: the block of each
   // column-wave's 16*NT columns.
-  __shared__ float lsw[2][kMaxSlices];
+  constexpr int kScaleSets = GATEUP ? 2 : WN;
+  __shared__ float lsw[kScaleSets][kMaxSlices];
   if constexpr (kScaled) {
-    for (int i = tid; i < 2 * p.nKb; i += 256) {
+    for (int i = tid; i < kScaleSets * p.nKb; i += kThreads) {
       const int w = i / p.nKb, sl = i - w * p.nKb;
       if (GATEUP) {
         lsw[w][sl] = (w == 0 ? gv.s0 : gv.s1)[(int64_t)(ncol0 >> 7) * p.nKb + sl];
@@ -226,15 +246,15 @@ __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gem
     uint8_t* st = stage_ptr(uc);
     const int64_t off = (int64_t)s * 128;
 #pragma unroll
-    for (int i = 0; i < kInstA; ++i) lds_copy16(p.a + srcA[i] + off, st + (8 * (4 * i + wave)) * 128);
+    for (int i = 0; i < kInstA; ++i) lds_copy16(p.a + srcA[i] + off, st + (8 * (kWaves * i + wave)) * 128);
 #pragma unroll
-    for (int i = 0; i < kInstB; ++i) lds_copy16(srcB[i] + off, st + (kBM + 8 * (4 * i + wave)) * 128);
+    for (int i = 0; i < kInstB; ++i) lds_copy16(srcB[i] + off, st + (kBM + 8 * (kWaves * i + wave)) * 128);
     if (kScaled && wave < 2) lds_copy4(p.a_scales + srcS + s, scale_ptr(uc) + 64 * wave);
   };
 
-  // A tile of at most 64 rows (the last tile of a group) runs with 2 row
-  // subtiles per wave (wave rows 32 wm .. 32 wm + 31) instead of 4, halving its
-  // MFMA and conversion work; the copies are the same.
+  // A tile of r < 128 rows (the last tile of a group) runs with MT =
+  // ceil(r / 32) row subtiles per wave (wave rows 16 MT wm .. 16 MT wm + 16 MT - 1)
+  // instead of 4; the copies are the same.
   auto run = [&](auto mtc) {
     constexpr int MT = decltype(mtc)::value;
     f32x4 acc[MT][NT];
@@ -246,7 +266,7 @@ __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gem
     // weight rows (within the weight region) of this lane's subtiles; the
     // weight fragment is the first MFMA operand, the A fragment the second
     auto brow = [&](int j) -> int {
-      if (GATEUP) return (j < NH ? 0 : 16 * NT) + wn * 16 * NH + 16 * (j % NH) + r16;
+      if (GATEUP) return (j < NH ? 0 : kHalfB) + wn * 16 * NH + 16 * (j % NH) + r16;
       return wn * 16 * NT + 16 * j + r16;
     };
 
@@ -394,8 +414,16 @@ __global__ __launch_bounds__(256, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) void gem
       }
     }
   };
+#if DMOE_TILE_MT_FINE
+  const int rows = m_end - m0;
+  if (rows <= 32) run(std::integral_constant<int, 1>{});
+  else if (rows <= 64) run(std::integral_constant<int, 2>{});
+  else if (rows <= 96) run(std::integral_constant<int, 3>{});
+  else run(std::integral_constant<int, 4>{});
+#else
   if (m_end - m0 <= 64) run(std::integral_constant<int, 2>{});
   else run(std::integral_constant<int, 4>{});
+#endif
 }
 
 __global__ void fill_offsets_kernel(int32_t* offsets, int rows) {
@@ -477,18 +505,22 @@ static hipError_t launch_gemm(const GemmArgs& g, bool gateup, hipStream_t stream
     return launch_gemm_stream(p, g.dtype, gateup, (int)per_expert, (int)npad, g.E_loc, stream);
   }
   // tile kernel: 128-byte stages for every mode (FP8: one 128-wide slice, BF16: 64 elements)
-  constexpr int NS = DMOE_TILE_NS;
   constexpr int NT_GU = DMOE_TILE_NT_GATEUP, NT_DN = DMOE_TILE_NT_DOWN;
-  const int nt = gateup ? NT_GU : NT_DN;
-  const int nNB = gateup ? (int)(npad / (16 * nt)) : (int)ceil_div(npad, 32 * nt);
+  constexpr int WN_GU = DMOE_TILE_WN_GATEUP, WN_DN = DMOE_TILE_WN_DOWN;
+  constexpr int NS_GU = WN_GU == 2 ? DMOE_TILE_NS : DMOE_TILE_NS_WIDE;
+  constexpr int NS_DN = WN_DN == 2 ? DMOE_TILE_NS : DMOE_TILE_NS_WIDE;
+  // weight rows per workgroup: gate/up 8 NT WN gate + as many up rows (npad is a multiple of 128,
+  // and 8 NT WN divides 128); down 16 NT WN (a partial last block leaves waves idle)
+  const int nNB = gateup ? (int)(npad / (8 * NT_GU * WN_GU)) : (int)ceil_div(npad, 16 * NT_DN * WN_DN);
   const unsigned grid = (unsigned)round_up((int64_t)cap * nNB, 8);
   const int nv = (int)npad;
+  const unsigned thr = 128 * (gateup ? WN_GU : WN_DN);
   if (g.dtype == DMOE_FP8_E4M3) {
-    if (gateup) gemm_tile_kernel<kModeFP8X, true, NS, NT_GU><<<grid, 256, 0, stream>>>(p, nNB, nv);
-    else gemm_tile_kernel<kModeFP8, false, NS, NT_DN><<<grid, 256, 0, stream>>>(p, nNB, nv);
+    if (gateup) gemm_tile_kernel<kModeFP8X, true, NS_GU, NT_GU, WN_GU><<<grid, thr, 0, stream>>>(p, nNB, nv);
+    else gemm_tile_kernel<kModeFP8, false, NS_DN, NT_DN, WN_DN><<<grid, thr, 0, stream>>>(p, nNB, nv);
   } else {
-    if (gateup) gemm_tile_kernel<kModeBF16, true, NS, NT_GU><<<grid, 256, 0, stream>>>(p, nNB, nv);
-    else gemm_tile_kernel<kModeBF16, false, NS, NT_DN><<<grid, 256, 0, stream>>>(p, nNB, nv);
+    if (gateup) gemm_tile_kernel<kModeBF16, true, NS_GU, NT_GU, WN_GU><<<grid, thr, 0, stream>>>(p, nNB, nv);
+    else gemm_tile_kernel<kModeBF16, false, NS_DN, NT_DN, WN_DN><<<grid, thr, 0, stream>>>(p, nNB, nv);
   }
   return hipGetLastError();
 }
