@@ -11,35 +11,53 @@ namespace dmoe {
 
 // ---------------------------------------------------------------------------
 // Weight-streaming kernel for few rows per expert (decode). A workgroup
-// owns 64 output columns of one group: WR = 128 weight rows for gate/up (64
-// gate + 64 up) or 64 for down. Every 128-byte K stage of those rows, of the
-// group's (up to 16 R) A rows and of their FP8 scales moves global -> LDS with
-// direct loads (each instruction covers 8 whole 128-byte lines) through a
-// kStageRing-deep ring; wave w then multiplies the 16 columns 16 w .. 16 w + 15
-// from LDS fragments. Grid: (ceil(N_pad / 64), E_loc + chunks).
+// owns WR weight rows of one group: down, 64 rows = 64 columns of o, wave w
+// multiplying columns 16 w .. 16 w + 15; gate/up, WR = 2 CW rows (CW gate rows,
+// then the CW up rows of the same columns of h). With CW = 64 every wave
+// multiplies the gate and the up rows of its 16 columns; with CW = 32 (the
+// default) waves 0, 1 multiply the gate rows and waves 2, 3 the up rows of
+// columns 16 (w & 1) .. + 15, and the up accumulators reach the gate waves
+// through LDS for the SwiGLU epilogue. Narrower workgroups halve the work per
+// workgroup, so the last partial round of workgroups (all do the same
+// weight traffic) costs half as much. Every 128-byte K stage of the rows, of
+// the group's (up to 16 R) A rows and of their FP8 scales moves global -> LDS
+// with direct loads (each instruction covers 8 whole 128-byte lines) through a
+// ring of kRingBF16 or kRingFP8 stages (a 128-byte BF16 stage holds half the K
+// of an FP8 one). Grid: (N_pad / CW, E_loc + chunks).
 // ---------------------------------------------------------------------------
-#ifndef DMOE_STAGE_RING
-#define DMOE_STAGE_RING 4
+#ifndef DMOE_STAGE_RING_BF16
+#define DMOE_STAGE_RING_BF16 6
 #endif
-constexpr int kStageRing = DMOE_STAGE_RING;
+#ifndef DMOE_STAGE_RING_FP8
+#define DMOE_STAGE_RING_FP8 4
+#endif
+#ifndef DMOE_STREAM_GATEUP_CW
+#define DMOE_STREAM_GATEUP_CW 32
+#endif
+constexpr int kRingBF16 = DMOE_STAGE_RING_BF16, kRingFP8 = DMOE_STAGE_RING_FP8;
+constexpr int kGateUpCW = DMOE_STREAM_GATEUP_CW;
+static_assert(kGateUpCW == 32 || kGateUpCW == 64, "gate/up column block");
 
 template <int DT, bool GATEUP, int R>
 __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n_cols) {
   constexpr bool kFP8 = DT == DMOE_FP8_E4M3;
-  constexpr int WR = GATEUP ? 128 : 64;   // weight rows per workgroup
+  constexpr int CW = GATEUP ? kGateUpCW : 64;  // output columns per workgroup
+  constexpr int WR = GATEUP ? 2 * CW : 64;     // weight rows per workgroup
+  constexpr bool kSplit = GATEUP && CW == 32;  // gate and up rows on different waves
   constexpr int AR = 16 * R;              // A rows per pass
   constexpr int kRows = WR + AR;
-  constexpr int NS = kStageRing;
+  constexpr int NS = kFP8 ? kRingFP8 : kRingBF16;
   constexpr int kCopies = WR / 32 + 1 + (kFP8 ? 1 : 0);  // direct copies per wave per stage
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][kRows * 128];
   __shared__ __attribute__((aligned(256))) float lsa[NS][32];
   __shared__ float lsw[2][kMaxSlices];
+  __shared__ f32x4 xup[kSplit ? 2 * R * 64 : 1];  // up accumulators of waves 2, 3
   asm volatile("" ::"v"(&ring[0][0]), "v"(&lsa[0][0]) : "memory");
 
   const GroupView gv = group_view(p, blockIdx.y);
   const int row_beg = gv.row_beg, row_end = gv.row_end;
   if (row_beg >= row_end) return;
-  const int n0 = blockIdx.x * 64;
+  const int n0 = blockIdx.x * CW;
   if (n0 >= n_cols) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -59,8 +77,8 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
 #pragma unroll
   for (int i = 0; i < WR / 32; ++i) {
     const int row = 8 * (4 * i + wave) + (lane >> 3);
-    const uint8_t* base = (GATEUP && row >= 64) ? gv.w1 : gv.w0;
-    srcB[i] = base + (int64_t)(n0 + (row & 63)) * p.ldw_b + 16 * swz(row, lane & 7);
+    const uint8_t* base = (GATEUP && row >= CW) ? gv.w1 : gv.w0;
+    srcB[i] = base + (int64_t)(n0 + row % CW) * p.ldw_b + 16 * swz(row, lane & 7);
   }
 
   for (int m0 = row_beg; m0 < row_end; m0 += AR) {
@@ -84,7 +102,8 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
       if (kFP8 && lane < 8) lds_copy4(srcS + s, &lsa[s % NS][8 * wave]);
     };
 
-    constexpr int NM = GATEUP ? 2 : 1;
+    // weight fragments per wave: gate and up (CW = 64), or one of them
+    constexpr int NM = (GATEUP && !kSplit) ? 2 : 1;
     f32x4 acc[NM][R];
 #pragma unroll
     for (int t = 0; t < NM; ++t)
@@ -97,7 +116,7 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
       i32x4 fb[NM][2], fa[R][2];
 #pragma unroll
       for (int t = 0; t < NM; ++t) {
-        const int row = 64 * t + 16 * wave + r16;
+        const int row = 64 * t + 16 * wave + r16;  // kSplit: rows 16 wave .. (gate, then up)
         fb[t][0] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4));
         fb[t][1] = *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4 + 1));
       }
@@ -128,7 +147,7 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
             for (int k4 = 0; k4 < 4; ++k4)
               part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b16[t][k4]),
                                                              __builtin_bit_cast(bf16x8, a16[k4]), part, 0, 0, 0);
-            const float saw = sa * lsw[t][s];
+            const float saw = sa * lsw[kSplit ? wave >> 1 : t][s];
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[t][i][q] = fmaf(part[q], saw, acc[t][i][q]);
           }
@@ -174,7 +193,23 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
       stage_barrier();  // buffer s % NS may be refilled
     }
 
-    // ---- epilogue: lane (r16, g4) holds row m0 + 16 i + r16, columns n0 + 16 wave + 4 g4 + q ----
+    // ---- epilogue: lane (r16, g4) holds row m0 + 16 i + r16, columns n0 + 16 wave' + 4 g4 + q
+    // (wave' = wave, or wave & 1 when the gate and up rows sit on different waves) ----
+    f32x4 up[R];
+    if constexpr (kSplit) {
+      // the previous pass's readers of xup finished before the stage barriers of this pass
+      if (wave >= 2) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) xup[((wave - 2) * R + i) * 64 + lane] = acc[0][i];
+      }
+      __syncthreads();
+      if (wave >= 2) continue;
+#pragma unroll
+      for (int i = 0; i < R; ++i) up[i] = xup[(wave * R + i) * 64 + lane];
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i) up[i] = acc[NM - 1][i];
+    }
     const bool wide = (p.ldo & 3) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 7) == 0;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -182,9 +217,9 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
       if (m >= row_end) continue;
       float v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = GATEUP ? silu(acc[0][i][q]) * acc[NM - 1][i][q] : acc[0][i][q];
+      for (int q = 0; q < 4; ++q) v[q] = GATEUP ? silu(acc[0][i][q]) * up[i][q] : acc[0][i][q];
       const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-      uint16_t* o = p.out + (int64_t)m * p.ldo + n0 + 16 * wave + 4 * g4;
+      uint16_t* o = p.out + (int64_t)m * p.ldo + n0 + 16 * (kSplit ? wave & 1 : wave) + 4 * g4;
       if (wide) {
         *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
       } else {
@@ -203,7 +238,8 @@ hipError_t launch_gemm_stream(const TileArgs& p, int dtype, bool gateup, int row
   const int R = rows_per_expert <= 16 ? 1 : 2;
   if (p.x_chunk != 16 * R) return hipErrorInvalidValue;
   const int xchunks = (int)ceil_div(p.x_rows, p.x_chunk);
-  const dim3 grid((unsigned)(n_pad / 64), (unsigned)(E_loc + xchunks));
+  const int cw = gateup ? kGateUpCW : 64;
+  const dim3 grid((unsigned)(n_pad / cw), (unsigned)(E_loc + xchunks));
 #define DMOE_STREAM(DTV, GU)                                                                         \
   do {                                                                                               \
     if (R == 1) gemm_stage_kernel<DTV, GU, 1><<<grid, 256, 0, stream>>>(p, n_pad);                   \
