@@ -116,15 +116,20 @@ def test_forward_is_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_all_tokens_on_one_expert_and_empty_experts():
-    """Every token's top-1 is expert 5; most experts get no rows at all."""
-    cfg = synth.LayerConfig("skew", T=200, H=512, F=256, F_s=256, E=32, E_loc=32, e0=0, K=2, dtype="fp8",
+@pytest.mark.parametrize("dtype,K", [("fp8", 2), ("bf16", 2), ("fp8", 4), ("bf16", 4)])
+def test_all_tokens_on_one_expert_and_empty_experts(dtype, K):
+    """Every token's top-1 is expert 5 and its next choices are the same 1 or 3 experts; the other experts get no
+    rows. The host bound on rows per expert (T*K/E = 13 or 25) selects the weight-streaming kernel with 16 or 32
+    rows per pass, so the 200-row experts take 13 or 7 passes."""
+    cfg = synth.LayerConfig("skew", T=200, H=512, F=256, F_s=256, E=32, E_loc=32, e0=0, K=K, dtype=dtype,
                             T_s=0, logits="uniform")
     layer = build_layer(cfg)
     x_bits = synth.x_bf16(cfg)
     L = np.full((cfg.T, cfg.E), -5.0, np.float32)
     L[:, 5] = 3.0
     L[:, 9] = np.linspace(-1, 1, cfg.T).astype(np.float32)
+    L[:, 12] = np.linspace(-2, -1.5, cfg.T).astype(np.float32)
+    L[:, 20] = -3.0
     ref = oracle.moe_forward(cfg, x_bits, weights_provider(cfg), logits=L)
     _check_given_logits_path(cfg, layer, to_dev_bf16(x_bits), ref, L)
 
