@@ -206,9 +206,15 @@ size_t dmoe_gemm_ws_bytes(int32_t max_rows, int32_t E_loc) {
   return gemm_ws_bytes(max_rows, E_loc);
 }
 
+// The tile GEMM addresses every operand as a base plus a 32-bit byte offset.
+static bool span_fits(int64_t rows, int64_t ld, int64_t es) { return rows * ld * es <= (int64_t(1) << 32); }
+
+// a_rows: rows of a the call can read (< 0: not known on the host, the
+// caller's row_token must stay within 4 GiB of a).
 static dmoe_status check_gemm_common(int dtype, const void* a, int64_t lda, const float* a_scales, int64_t ldas,
-                                     const int32_t* offsets, int E_loc, int max_rows, int Kdim,
-                                     const void* w0, int64_t ldw, const float* ws0, void* ws, size_t ws_bytes) {
+                                     const int32_t* offsets, int E_loc, int max_rows, int Kdim, int Ndim,
+                                     int64_t a_rows, const void* w0, int64_t ldw, const float* ws0, void* ws,
+                                     size_t ws_bytes) {
   TRY(check_dtype(dtype));
   REQ(E_loc >= 1 && E_loc <= 1024, DMOE_ERR_INVALID_ARG, "E_loc = %d outside [1, 1024]", E_loc);
   REQ(max_rows >= 0, DMOE_ERR_INVALID_ARG, "max_rows < 0");
@@ -226,6 +232,9 @@ static dmoe_status check_gemm_common(int dtype, const void* a, int64_t lda, cons
     REQ(ldas >= ceil_div(Kdim, 128), DMOE_ERR_INVALID_ARG, "ldas below ceil(K/128)");
     REQ(Kdim <= 16384, DMOE_ERR_UNSUPPORTED, "FP8 reduction length %d above 16384", Kdim);
   }
+  REQ(span_fits(round_up(Ndim, 128), ldw, es), DMOE_ERR_UNSUPPORTED, "one expert's weights span 4 GiB or more");
+  REQ(a_rows < 0 || (span_fits(a_rows, lda, es) && span_fits(a_rows, ldas, 4)), DMOE_ERR_UNSUPPORTED,
+      "the activation operand spans 4 GiB or more");
   REQ(ws != nullptr && ws_bytes >= gemm_ws_bytes(max_rows, E_loc), DMOE_ERR_WORKSPACE,
       "gemm workspace needs %zu bytes, got %zu", gemm_ws_bytes(max_rows, E_loc), ws_bytes);
   return DMOE_OK;
@@ -239,8 +248,8 @@ dmoe_status dmoe_grouped_gemm_gateup(int32_t dtype, const void* a, int64_t lda, 
                                      hipStream_t stream) {
   REQ(H > 0 && H % 128 == 0, DMOE_ERR_INVALID_ARG, "H = %d must be a positive multiple of 128", H);
   REQ(F > 0 && F % 8 == 0, DMOE_ERR_INVALID_ARG, "F = %d must be a positive multiple of 8", F);
-  TRY(check_gemm_common(dtype, a, lda, a_scales, ldas, offsets, E_loc, max_rows, H, w_gate, ldw, w_scales_gate, ws,
-                        ws_bytes));
+  TRY(check_gemm_common(dtype, a, lda, a_scales, ldas, offsets, E_loc, max_rows, H, F, row_token ? -1 : max_rows,
+                        w_gate, ldw, w_scales_gate, ws, ws_bytes));
   REQ_PTR(w_up, "w_up");
   REQ_AL(w_up, "w_up");
   if (dtype == DMOE_FP8_E4M3) REQ_PTR(w_scales_up, "w_scales_up");
@@ -258,8 +267,8 @@ dmoe_status dmoe_grouped_gemm_down(int32_t dtype, const void* h, int64_t ldh, co
                                    int64_t ldo, void* ws, size_t ws_bytes, hipStream_t stream) {
   REQ(H > 0 && H % 128 == 0, DMOE_ERR_INVALID_ARG, "H = %d must be a positive multiple of 128", H);
   REQ(F > 0 && F % 8 == 0, DMOE_ERR_INVALID_ARG, "F = %d must be a positive multiple of 8", F);
-  TRY(check_gemm_common(dtype, h, ldh, h_scales, ldhs, offsets, E_loc, max_rows, F, w_down, ldw, w_scales_down, ws,
-                        ws_bytes));
+  TRY(check_gemm_common(dtype, h, ldh, h_scales, ldhs, offsets, E_loc, max_rows, F, H, max_rows, w_down, ldw,
+                        w_scales_down, ws, ws_bytes));
   REQ_PTR(o, "o");
   REQ_AL(o, "o");
   TRY(check_pitch(ldo, H, 2, "ldo"));
@@ -355,6 +364,9 @@ dmoe_status dmoe_shared_expert(int32_t dtype, const void* a, int64_t lda, const 
     REQ(a_scales && w_scales_gate && w_scales_up && w_scales_down, DMOE_ERR_INVALID_ARG, "FP8 scales missing");
     REQ(ldas >= H / 128, DMOE_ERR_INVALID_ARG, "ldas below H/128");
   }
+  REQ(span_fits(T_s, lda, es) && span_fits(T_s, ldas, 4) && span_fits(round_up(F_s, 128), ldw_gu, es) &&
+          span_fits(H, ldw_d, es) && span_fits(T_s, round_up(F_s, 128), 2),
+      DMOE_ERR_UNSUPPORTED, "an operand spans 4 GiB or more");
   const size_t need = dmoe_shared_expert_ws_bytes(dtype, T_s, H, F_s);
   REQ(ws != nullptr && aligned16(ws) && ws_bytes >= need, DMOE_ERR_WORKSPACE,
       "shared expert workspace needs %zu bytes, got %zu", need, ws_bytes);
@@ -507,6 +519,15 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
   REQ_PTR(p->y, "y");
   REQ_AL(p->y, "y");
   TRY(check_pitch(p->ldy, d->H, 2, "ldy"));
+  {
+    // every GEMM operand within 4 GiB of its base (32-bit offsets in the tile GEMM)
+    const int64_t rows = (int64_t)d->T * d->K + d->T_s;
+    const int64_t fspad = round_up(d->F_s, 128);
+    REQ(span_fits(d->T, fp8 ? d->H : p->ldx, fp8 ? 1 : 2) && span_fits(rows, fpad, 2) &&
+            span_fits(fpad, p->ldw_gu, es) && span_fits(d->H, p->ldw_d, es) &&
+            (!shared || (span_fits(fspad, p->ldsw_gu, es) && span_fits(d->H, p->ldsw_d, es))),
+        DMOE_ERR_UNSUPPORTED, "an operand spans 4 GiB or more");
+  }
   const FwdLayout L = fwd_layout(d);
   REQ(ws != nullptr && aligned16(ws) && ws_bytes >= (size_t)L.total, DMOE_ERR_WORKSPACE,
       "forward workspace needs %lld bytes, got %zu", (long long)L.total, ws_bytes);

@@ -242,14 +242,32 @@ __global__ __launch_bounds__(128 * WN, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) voi
   }
   __syncthreads();
 
+  // Copies address their source as a wave-uniform base (SGPRs) plus a 32-bit
+  // per-lane byte offset: advancing a stage is a scalar add. Every offset
+  // fits in 32 bits because each operand spans less than 4 GiB (checked by the
+  // entry points; a caller-supplied row_token must stay within that span).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t aoff[kInstA], boff[kInstB];
+#pragma unroll
+  for (int i = 0; i < kInstA; ++i) aoff[i] = (uint32_t)srcA[i];
+  const uint8_t* bb0 = uniform_ptr(GATEUP ? gv.w0 + (int64_t)ncol0 * p.ldw_b : gv.w0);
+  const uint8_t* bb1 = uniform_ptr(GATEUP ? gv.w1 + (int64_t)ncol0 * p.ldw_b : gv.w0);
+  static_assert(!GATEUP || kHalfB % (8 * kWaves) == 0, "a copy covers gate rows or up rows only");
+#pragma unroll
+  for (int i = 0; i < kInstB; ++i)
+    boff[i] = (uint32_t)(srcB[i] - ((GATEUP && 8 * kWaves * i >= kHalfB) ? bb1 : bb0));
+  const uint32_t soff = (uint32_t)(srcS * 4);
   auto issue = [&](auto uc, int s) {
-    uint8_t* st = stage_ptr(uc);
+    const uint32_t st = (uint32_t)(uintptr_t)stage_ptr(uc);
     const int64_t off = (int64_t)s * 128;
 #pragma unroll
-    for (int i = 0; i < kInstA; ++i) lds_copy16(p.a + srcA[i] + off, st + (8 * (kWaves * i + wave)) * 128);
+    for (int i = 0; i < kInstA; ++i) lds_copy16_s(p.a + off, aoff[i], st + (8 * kWaves * i + 8 * wave_u) * 128);
 #pragma unroll
-    for (int i = 0; i < kInstB; ++i) lds_copy16(srcB[i] + off, st + (kBM + 8 * (kWaves * i + wave)) * 128);
-    if (kScaled && wave < 2) lds_copy4(p.a_scales + srcS + s, scale_ptr(uc) + 64 * wave);
+    for (int i = 0; i < kInstB; ++i)
+      lds_copy16_s(((GATEUP && 8 * kWaves * i >= kHalfB) ? bb1 : bb0) + off, boff[i],
+                   st + (kBM + 8 * kWaves * i + 8 * wave_u) * 128);
+    if (kScaled && wave < 2)
+      lds_copy4_s(p.a_scales + s, soff, (uint32_t)(uintptr_t)scale_ptr(uc) + 256 * wave_u);
   };
 
   // A tile of r < 128 rows (the last tile of a group) runs with MT =

@@ -127,6 +127,16 @@ __device__ __forceinline__ void lds_copy4(const void* gptr, const void* lds_base
   asm volatile("global_load_lds_dword %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
 }
 
+// The same copies with the global address split into a wave-uniform 64-bit base
+// (SGPRs) and a per-lane 32-bit byte offset, so that moving to the next stage
+// is a scalar add and the per-lane offsets stay in place.
+__device__ __forceinline__ void lds_copy16_s(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void lds_copy4_s(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
 // Workgroup barrier without the memory fence of __syncthreads (whose release
 // half would wait for every outstanding global load, including the younger
 // pipeline stages). Callers order memory with explicit s_waitcnt first; the

@@ -31,6 +31,12 @@
  * - No entry point reads device memory from the host, so every call can be
  *   captured into a HIP graph. Grids are sized from host-known bounds and
  *   kernels read the actual counts on the device.
+ * - The grouped GEMMs address each operand as a base pointer plus a 32-bit
+ *   byte offset: the activation rows a call can read, one expert's weight
+ *   block and the activation scales must each span at most 4 GiB. Entry
+ *   points return DMOE_ERR_UNSUPPORTED when the sizes they are given break
+ *   this; for a gathered operand (row_token) the caller keeps the rows it
+ *   names within the first 4 GiB of `a`.
  *
  * Weight layout (produced once, before timing, by the preparation calls)
  * ------------------------------------------------------------------
@@ -197,6 +203,9 @@ dmoe_status dmoe_quant_weight_blocks(const float* w, int32_t rows, int32_t cols,
  * max_rows: host-side upper bound on offsets[E_loc] (T*K for routed rows); it
  * sizes the grid and the tile schedule, so it must not be below the real row
  * count (rows past the capacity it implies are not computed).
+ * row_token: every row it names satisfies (row + 1) * lda * element size <=
+ * 4 GiB (without row_token the check is max_rows * lda * element size, done
+ * here); DMOE_ERR_UNSUPPORTED when an expert's weights span more than 4 GiB.
  * ws: at least dmoe_gemm_ws_bytes(max_rows, E_loc).
  */
 size_t dmoe_gemm_ws_bytes(int32_t max_rows, int32_t E_loc);

@@ -78,6 +78,28 @@ def test_gemm_rejects_bad_dtype_and_shapes(L):
     assert lib.dmoe_grouped_gemm_gateup(2, *small_ws) == L._lib.DMOE_ERR_WORKSPACE
 
 
+def test_gemm_rejects_operands_spanning_4gib(L):
+    """The tile GEMM addresses operands as base + 32-bit offset; larger spans are refused before any launch."""
+    lib = L.lib()
+    f = 0x1000
+    BF16 = 1
+    max_rows, ldh = 2_000_000, 4096  # 2e6 rows x 4096 x 2 B = 16 GB of h
+    ws = lib.dmoe_gemm_ws_bytes(max_rows, 256)
+    st = lib.dmoe_grouped_gemm_down(BF16, f, ldh, None, 0, f, 256, max_rows, f, 1536, None, 1536, 5120, f, 5120, f,
+                                    ws, None)
+    assert st == L._lib.DMOE_ERR_UNSUPPORTED
+    assert b"4 GiB" in lib.dmoe_last_error()
+    # the same call with a small row bound passes validation up to the workspace check
+    st = lib.dmoe_grouped_gemm_down(BF16, f, ldh, None, 0, f, 256, 512, f, 1536, None, 1536, 5120, f, 5120, f, 16,
+                                    None)
+    assert st == L._lib.DMOE_ERR_WORKSPACE
+    # one expert's gate/up block of 1536 rows x 2^21 BF16 columns = 6.4 GB
+    ws = lib.dmoe_gemm_ws_bytes(512, 256)
+    st = lib.dmoe_grouped_gemm_gateup(BF16, f, 5120, None, 0, f, f, 256, 512, f, f, 1 << 21, None, None, 5120, 1536,
+                                      f, 1536, f, ws, None)
+    assert st == L._lib.DMOE_ERR_UNSUPPORTED
+
+
 def test_forward_desc_validation_and_sizes(L):
     d = L.LayerDesc(8192, 5120, 1536, 1536, 256, 256, 0, 8, 8192, 2, 0)
     n = L.dmoe_forward_ws_bytes(d)
