@@ -381,28 +381,69 @@ __global__ __launch_bounds__(128 * WN, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) voi
     constexpr int kCopies = kInstA + kInstB;  // per wave per stage, plus one scale copy on waves 0 and 1
     const int S = p.stages;
     const bool scale_wave = kScaled && wave < 2;
-    static_for<0, NS - 1>([&](auto uc) {
-      if (decltype(uc)::value < S) issue(uc, decltype(uc)::value);
-    });
-    for (int s0 = 0; s0 < S; s0 += NS) {
-      static_for<0, NS>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        const int s = s0 + u;
-        if (s < S) {
-          if (s + NS - 1 < S) {
-            issue(std::integral_constant<int, (u + NS - 1) % NS>{}, s + NS - 1);
-            // stage s is complete once at most the NS-1 younger stages are in flight
-            if (scale_wave) wait_vmcnt<(kCopies + 1) * (NS - 1)>();
-            else wait_vmcnt<kCopies * (NS - 1)>();
-          } else {
-            wait_vmcnt<0>();
-          }
-          stage_barrier();  // every wave's copies of stage s have landed in LDS
-          if (active) compute(uc, s);
-          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
-          stage_barrier();  // buffer u may be refilled
-        }
+    // Two schedules. One barrier per stage (gate/up and BF16 down): the ring
+    // starts full (stages 0 .. NS-1) and stage s + NS - 1 is issued once every
+    // wave has passed the barrier of stage s, i.e. is done with stage s - 1,
+    // whose buffer it refills. Two barriers per stage (FP8 down, whose stages
+    // hold little MFMA work and wait on first-touch weight reads): stage
+    // s + NS - 1 is issued before the wait for stage s, right after the barrier
+    // that releases buffer (s - 1) % NS, which keeps one more stage's latency
+    // covered; measured faster there, slower for the others.
+    constexpr bool kOneBarrier = GATEUP || MODE == kModeBF16;
+    if constexpr (!kOneBarrier) {
+      static_for<0, NS - 1>([&](auto uc) {
+        if (decltype(uc)::value < S) issue(uc, decltype(uc)::value);
       });
+      for (int s0 = 0; s0 < S; s0 += NS) {
+        static_for<0, NS>([&](auto uc) {
+          constexpr int u = decltype(uc)::value;
+          const int s = s0 + u;
+          if (s < S) {
+            if (s + NS - 1 < S) {
+              issue(std::integral_constant<int, (u + NS - 1) % NS>{}, s + NS - 1);
+              // stage s is complete once at most the NS-1 younger stages are in flight
+              if (scale_wave) wait_vmcnt<(kCopies + 1) * (NS - 1)>();
+              else wait_vmcnt<kCopies * (NS - 1)>();
+            } else {
+              wait_vmcnt<0>();
+            }
+            stage_barrier();  // every wave's copies of stage s have landed in LDS
+            if (active) compute(uc, s);
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
+            stage_barrier();  // buffer u may be refilled
+          }
+        });
+      }
+    } else {
+      static_for<0, NS>([&](auto uc) {
+        if (decltype(uc)::value < S) issue(uc, decltype(uc)::value);
+      });
+      for (int s0 = 0; s0 < S; s0 += NS) {
+        static_for<0, NS>([&](auto uc) {
+          constexpr int u = decltype(uc)::value;
+          const int s = s0 + u;
+          if (s < S) {
+            // stage s is complete once at most the stages issued after it are in flight:
+            // s+1 .. s+NS-1 at s = 0 (the full ring), s+1 .. s+NS-2 afterwards
+            const int younger = min(S - 1, s == 0 ? NS - 1 : s + NS - 2) - s;
+            if (younger >= NS - 1) {
+              if (scale_wave) wait_vmcnt<(kCopies + 1) * (NS - 1)>();
+              else wait_vmcnt<kCopies * (NS - 1)>();
+            } else if (NS > 2 && younger >= NS - 2) {
+              if (scale_wave) wait_vmcnt<(kCopies + 1) * (NS > 2 ? NS - 2 : 0)>();
+              else wait_vmcnt<kCopies * (NS > 2 ? NS - 2 : 0)>();
+            } else {
+              wait_vmcnt<0>();
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage s-1 are done
+            // one barrier per stage: every wave's copies of stage s have landed, and every wave is done
+            // with buffer (s-1) % NS, which the copies of stage s+NS-1 refill
+            stage_barrier();
+            if (s > 0 && s + NS - 1 < S) issue(std::integral_constant<int, (u + NS - 1) % NS>{}, s + NS - 1);
+            if (active) compute(uc, s);
+          }
+        });
+      }
     }
 
     if (!active) return;
