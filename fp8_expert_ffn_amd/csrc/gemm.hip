@@ -83,9 +83,10 @@ constexpr int kModeBF16 = 0, kModeFP8X = 1, kModeFP8 = 2;
 // with direct (asynchronous, register-free) loads through an NS-stage ring; a
 // stage is 128 bytes of every A and weight row (one 128-wide FP8 scale slice,
 // or 64 BF16 elements) plus the A rows' activation scales. LDS rows are 128
-// bytes, 16-byte units XOR-swizzled by (row >> 1) & 7 so that the 16 rows a
-// fragment read touches hit distinct banks. Grid: 1-D, tile-major, column
+// bytes with 16-byte units XOR-swizzled (swz in gemm_common.h) so that the
+// fragment reads are free of bank conflicts. Grid: 1-D, tile-major, column
 // block fastest.
+
 // Wave-uniform copy of a pointer (lets the compiler use scalar loads through it).
 template <typename T>
 __device__ __forceinline__ const T* uniform_ptr(const T* p) {
@@ -95,6 +96,11 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
 }
 
+// Build-time tuning knobs; the defaults are the measured best on gfx950 (the
+// alternatives stay buildable for re-measurement): ring depth NS (2 with two
+// workgroups per CU), waves per SIMD, an XCD-contiguous work order, column
+// tiles per wave NT, column waves WN (and the ring depth used with WN = 4), and
+// the ceil(rows / 32) row subtiles for short tiles.
 #ifndef DMOE_TILE_NS
 #define DMOE_TILE_NS 2
 #endif
