@@ -47,6 +47,14 @@ CASES = {
                                          dtype="fp8", T_s=0, logits="single"),
     "dense_small_bf16": synth.LayerConfig("dense_small_bf16", T=100, H=512, F=2304, F_s=0, E=1, E_loc=1, e0=0,
                                           K=1, dtype="bf16", T_s=0, logits="single"),
+    # shortest reductions on the tile GEMM (about 128 rows per expert): one or two 128-byte K stages,
+    # i.e. the pipeline's prologue and drain without a steady state
+    "min_k_fp8": synth.LayerConfig("min_k_fp8", T=256, H=128, F=128, F_s=128, E=4, E_loc=4, e0=0, K=2,
+                                   dtype="fp8", T_s=256, logits="router"),
+    "min_k_bf16": synth.LayerConfig("min_k_bf16", T=256, H=128, F=120, F_s=64, E=4, E_loc=4, e0=0, K=2,
+                                    dtype="bf16", T_s=256, logits="router"),
+    "short_k_fp8": synth.LayerConfig("short_k_fp8", T=300, H=256, F=200, F_s=200, E=5, E_loc=5, e0=0, K=2,
+                                     dtype="fp8", T_s=100, logits="uniform"),
 }
 
 
