@@ -55,6 +55,11 @@ CASES = {
                                     dtype="bf16", T_s=256, logits="router"),
     "short_k_fp8": synth.LayerConfig("short_k_fp8", T=300, H=256, F=200, F_s=200, E=5, E_loc=5, e0=0, K=2,
                                      dtype="fp8", T_s=100, logits="uniform"),
+    # 33..64 rows per expert on average (the tile GEMM with one short tile per expert)
+    "mid_rows_bf16": synth.LayerConfig("mid_rows_bf16", T=256, H=512, F=256, F_s=256, E=32, E_loc=32, e0=0, K=6,
+                                       dtype="bf16", T_s=200, logits="router"),
+    "mid_rows_nondiv_fp8": synth.LayerConfig("mid_rows_fp8", T=512, H=1024, F=1400, F_s=1400, E=64, E_loc=64, e0=0,
+                                             K=8, dtype="fp8", T_s=512, logits="uniform"),
 }
 
 
@@ -124,11 +129,12 @@ def test_forward_is_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("dtype,K", [("fp8", 2), ("bf16", 2), ("fp8", 4), ("bf16", 4)])
+@pytest.mark.parametrize("dtype,K", [("fp8", 2), ("bf16", 2), ("fp8", 4), ("bf16", 4), ("fp8", 8), ("bf16", 8)])
 def test_all_tokens_on_one_expert_and_empty_experts(dtype, K):
-    """Every token's top-1 is expert 5 and its next choices are the same 1 or 3 experts; the other experts get no
-    rows. The host bound on rows per expert (T*K/E = 13 or 25) selects the weight-streaming kernel with 16 or 32
-    rows per pass, so the 200-row experts take 13 or 7 passes."""
+    """Every token's top-1 is expert 5 and its next choices are the same 1, 3 or 7 experts (K = 8: experts 9, 12,
+    20 and the four lowest-index experts among the equal rest); the other experts get no rows. The host bound on
+    rows per expert (T*K/E = 13, 25 or 50) selects the weight-streaming kernel with 16 or 32 rows per pass (the
+    200-row experts take 13 or 7 passes) or, at 50, the tile GEMM with two 128-row tiles per busy expert."""
     cfg = synth.LayerConfig("skew", T=200, H=512, F=256, F_s=256, E=32, E_loc=32, e0=0, K=K, dtype=dtype,
                             T_s=0, logits="uniform")
     layer = build_layer(cfg)
