@@ -77,12 +77,19 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
   __shared__ int32_t tot[1024];
   __shared__ int32_t partial[1024];
   __shared__ int32_t total;
+  // a thread walks one expert's column of counts, 16 independent loads in flight per step
+  constexpr int kChunk = 16;
   for (int e = threadIdx.x; e < E_loc; e += blockDim.x) {
     int32_t run = 0;
-    for (int b = 0; b < nblocks; ++b) {
-      const int32_t c = counts[(int64_t)b * E_loc + e];
-      counts[(int64_t)b * E_loc + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblocks; b0 += kChunk) {
+      int32_t c[kChunk];
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) c[j] = b0 + j < nblocks ? counts[(int64_t)(b0 + j) * E_loc + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        if (b0 + j < nblocks) counts[(int64_t)(b0 + j) * E_loc + e] = run;
+        run += c[j];
+      }
     }
     tot[e] = run;
   }
