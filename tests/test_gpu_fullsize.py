@@ -18,7 +18,7 @@ from gpu_util import (DEV, LOGIT_TOL, W_TOL, bf16_values, build_layer, compare_y
 
 pytestmark = pytest.mark.gpu
 
-SAMPLES = {1: 16, 2: 5, 3: 6, 4: 5, 5: 8, 6: 8, 7: 4}
+SAMPLES = {1: 16, 2: 5, 3: 6, 4: 5, 5: 8, 6: 8, 7: 4, 8: 10, 9: 6}
 
 
 def _sample_tokens(cfg, n):
@@ -31,7 +31,7 @@ def _sample_tokens(cfg, n):
     return np.array(sorted(picks))
 
 
-@pytest.mark.parametrize("ci", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("ci", [1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_full_size_workload(ci):
     cfg = synth.config(ci)
     say(f"[full size {ci}] {cfg}")
