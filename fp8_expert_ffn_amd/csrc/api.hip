@@ -402,7 +402,7 @@ dmoe_status dmoe_combine(const uint16_t* o, int64_t ldo, const int32_t* token_ro
 // ---------------------------------------------------------------------------
 namespace {
 enum { W_OFFSETS, W_ROW_TOKEN, W_ROW_SLOT, W_TOKEN_ROW, W_XQ, W_XS, W_H, W_HQ, W_HS, W_O, W_S, W_PERM, W_GEMM,
-       W_SHARED, W_COUNT };
+       W_SHARED, W_RSPLIT, W_COUNT };
 
 struct FwdLayout {
   int64_t off[W_COUNT];
@@ -412,6 +412,9 @@ struct FwdLayout {
 // The shared expert joins the routed GEMM launches as one extra group when its
 // width equals the routed width; its rows then follow the T*K routed rows in h and o.
 bool fuse_shared(const dmoe_layer_desc* d) { return d->T_s > 0 && d->F_s > 0 && d->F_s == d->F; }
+
+// Many tokens: the router runs as a tiled GEMM over W_r split once into BF16 parts.
+bool router_tiled(const dmoe_layer_desc* d) { return !d->logits_given && d->T > 256; }
 
 FwdLayout fwd_layout(const dmoe_layer_desc* d) {
   FwdLayout L;
@@ -436,6 +439,7 @@ FwdLayout fwd_layout(const dmoe_layer_desc* d) {
       (int64_t)permute_ws_bytes(d->T, d->K, d->E_loc),
       (int64_t)gemm_ws_bytes((int)mcap, d->E_loc, fused ? d->T_s : 0),
       (shared && !fused) ? shared_layout(d->dtype, d->T_s, d->H, d->F_s).total : -1,
+      router_tiled(d) ? (int64_t)router_split_bytes(d->E, d->H) : -1,
   };
   int64_t at = 0;
   for (int i = 0; i < W_COUNT; ++i) {
@@ -523,7 +527,8 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
     // every GEMM operand within 4 GiB of its base (32-bit offsets in the tile GEMM)
     const int64_t rows = (int64_t)d->T * d->K + d->T_s;
     const int64_t fspad = round_up(d->F_s, 128);
-    REQ(span_fits(d->T, fp8 ? d->H : p->ldx, fp8 ? 1 : 2) && span_fits(rows, fpad, 2) &&
+    REQ(span_fits(d->T, fp8 ? d->H : p->ldx, fp8 ? 1 : 2) && (!router_tiled(d) || span_fits(d->T, p->ldx, 2)) &&
+            span_fits(rows, fpad, 2) &&
             span_fits(fpad, p->ldw_gu, es) && span_fits(d->H, p->ldw_d, es) &&
             (!shared || (span_fits(fspad, p->ldsw_gu, es) && span_fits(d->H, p->ldsw_d, es))),
         DMOE_ERR_UNSUPPORTED, "an operand spans 4 GiB or more");
@@ -556,7 +561,10 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
 
   STEP(mark(), "event");
   if (!d->logits_given)
-    STEP(launch_router_logits(p->x, p->ldx, p->w_router, d->T, d->H, d->E, p->logits, stream), "router_logits");
+    STEP(router_tiled(d) ? launch_router_logits_split(p->x, p->ldx, p->w_router, d->T, d->H, d->E,
+                                                      reinterpret_cast<uint16_t*>(at(W_RSPLIT)), p->logits, stream)
+                         : launch_router_logits(p->x, p->ldx, p->w_router, d->T, d->H, d->E, p->logits, stream),
+         "router_logits");
   STEP(mark(), "event");
   {
     const int g = d->n_group <= 1 ? 1 : d->n_group;

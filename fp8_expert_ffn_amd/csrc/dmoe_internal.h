@@ -17,6 +17,11 @@ inline int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }
 // route.hip
 hipError_t launch_router_logits(const uint16_t* x, int64_t ldx, const float* w_r, int T, int H, int E,
                                 float* logits, hipStream_t stream);
+// Many tokens: W_r split once into its BF16 parts in `wsplit` (router_split_bytes)
+// and a tiled BF16 GEMM; requires H % 64 == 0 and T * ldx * 2 <= 4 GiB.
+size_t router_split_bytes(int E, int H);
+hipError_t launch_router_logits_split(const uint16_t* x, int64_t ldx, const float* w_r, int T, int H, int E,
+                                      uint16_t* wsplit, float* logits, hipStream_t stream);
 // n_group <= 1: ungrouped; renormalize: divide by the selected experts' sum (norm_topk_prob)
 hipError_t launch_route(const float* logits, int T, int E, int K, int n_group, int topk_group, bool renormalize,
                         float scaling, int32_t* ids, float* w, hipStream_t stream);

@@ -6,7 +6,7 @@
 // (num_experts_per_tok, norm_topk_prob, routed_scaling_factor, n_group,
 // topk_group); the softmax scoring is the reading of the docs' "post-softmax"
 // router_logits entry.
-#include "dmoe_internal.h"
+#include "gemm_common.h"
 
 namespace dmoe {
 
@@ -143,6 +143,154 @@ hipError_t launch_router_logits(const uint16_t* x, int64_t ldx, const float* w_r
     dim3 grid((T + 63) / 64, (E + 63) / 64);
     router_logits_kernel<4, 4, 4><<<grid, 256, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Router logits for many tokens as a tiled GEMM. W_r is split once per call
+// into its three BF16 parts (router_split_kernel: row e of `wsplit` holds hi,
+// then mid, then lo of W_r row e, H values each), so the GEMM itself is pure
+// BF16 matrix-core work: L = x.hi^T + x.mid^T + x.lo^T with FP32 accumulation,
+// three MFMAs per 32-wide K block as in router_logits_kernel.
+//
+// Workgroup tile: 64 tokens x 64 experts, 4 waves; wave (wm, wn) computes
+// tokens 32 wm .. +31 x experts 32 wn .. +31 as 2 x 2 MFMA tiles (the weight
+// fragment first, so each lane ends with one token and 4 consecutive experts).
+// Each stage is 64 K: 128 bytes of the 64 x rows and of the 3 x 64 weight rows
+// (part-major), moved global -> LDS with direct loads through a 2-stage ring
+// (32 KB per stage: two workgroups share a CU), one barrier per stage.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ w_r, int E, int H,
+                                                           uint16_t* __restrict__ wsplit) {
+  const int64_t n8 = (int64_t)E * H / 8;  // groups of 8 consecutive values (H % 8 == 0: one row each)
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < n8; g += (int64_t)gridDim.x * 256) {
+    const int64_t i = g * 8;
+    const int e = (int)(i / H), h = (int)(i - (int64_t)e * H);
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(w_r + i);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(w_r + i + 4);
+    const float w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    bf16x8 hi, mid, lo;
+    split3_bf16(w, hi, mid, lo);
+    uint16_t* row = wsplit + (int64_t)e * 3 * H + h;
+    *reinterpret_cast<bf16x8*>(row) = hi;
+    *reinterpret_cast<bf16x8*>(row + H) = mid;
+    *reinterpret_cast<bf16x8*>(row + 2 * H) = lo;
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void router_gemm_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                             const uint16_t* __restrict__ wsplit, int T, int H, int E,
+                                                             float* __restrict__ logits) {
+  constexpr int kX = 64, kW = 3 * 64, kRows = kX + kW;  // 128-byte LDS rows per stage
+  constexpr int kInst = kRows / 32;                     // direct copies per wave per stage (8 rows each)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kRows * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kRows * 128];
+  asm volatile("" ::"v"(lds0), "v"(lds1) : "memory");
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int S = H / 64;
+
+  // copy i of wave w fills LDS rows 8 (4 i + w) .. + 7: x rows first, then the
+  // weight rows part by part (LDS row 64 + 64 p + k holds part p of expert e0 + k)
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(wsplit);
+  uint32_t off[kInst];
+#pragma unroll
+  for (int i = 0; i < kInst; ++i) {
+    const int row = 8 * (4 * i + wave) + (lane >> 3);
+    const int c = 16 * swz(row, lane & 7);
+    if (row < kX) {
+      const int t = t0 + row < T ? t0 + row : 0;
+      off[i] = (uint32_t)((int64_t)t * ldx * 2 + c);
+    } else {
+      const int pr = row - kX, part = pr / 64, k = pr % 64;
+      const int e = e0 + k < E ? e0 + k : 0;
+      off[i] = (uint32_t)(((int64_t)e * 3 + part) * H * 2 + c);
+    }
+  }
+  auto issue = [&](uint8_t* st, int s) {
+    const int64_t o = (int64_t)s * 128;
+#pragma unroll
+    for (int i = 0; i < kInst; ++i)
+      lds_copy16_s((8 * 4 * i < kX ? xb : wb) + o, off[i], (uint32_t)(uintptr_t)st + (8 * 4 * i + 8 * wave_u) * 128);
+  };
+  static_assert(kX % 32 == 0, "a copy covers x rows or weight rows only");
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto frag = [&](const uint8_t* st, int row, int kb) -> bf16x8 {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(st + row * 128 + 16 * swz(row, 2 * g4 + kb)));
+  };
+  auto compute = [&](const uint8_t* st) {
+    bf16x8 fx[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) fx[i][kb] = frag(st, 32 * wm + 16 * i + r16, kb);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x8 fw[3][2];
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) fw[part][kb] = frag(st, kX + 64 * part + 32 * wn + 16 * j + r16, kb);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int part = 0; part < 3; ++part)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[part][kb], fx[i][kb], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // 2-stage ring, full at start; stage s + 1 is issued once every wave has
+  // passed the barrier of stage s (done with stage s - 1, whose buffer it refills)
+  issue(lds0, 0);
+  if (S > 1) issue(lds1, 1);
+  for (int s = 0; s < S; ++s) {
+    if (s == 0 && S > 1) wait_vmcnt<kInst>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage s-1 are done
+    stage_barrier();
+    if (s > 0 && s + 1 < S) issue((s & 1) ? lds0 : lds1, s + 1);
+    compute((s & 1) ? lds1 : lds0);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + 32 * wm + 16 * i + r16;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = e0 + 32 * wn + 16 * j + 4 * g4;
+      float* out = logits + (int64_t)t * E + e;
+      if ((E & 3) == 0 && e + 3 < E) {
+        *reinterpret_cast<f32x4*>(out) = acc[i][j];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (e + q < E) out[q] = acc[i][j][q];
+      }
+    }
+  }
+}
+
+size_t router_split_bytes(int E, int H) { return (size_t)E * 3 * H * 2; }
+
+hipError_t launch_router_logits_split(const uint16_t* x, int64_t ldx, const float* w_r, int T, int H, int E,
+                                      uint16_t* wsplit, float* logits, hipStream_t stream) {
+  const int64_t n8 = (int64_t)E * H / 8;
+  const unsigned sgrid = (unsigned)std::min<int64_t>(ceil_div(n8, 256), 2048);
+  router_split_kernel<<<sgrid, 256, 0, stream>>>(w_r, E, H, wsplit);
+  dim3 grid((unsigned)ceil_div(T, 64), (unsigned)ceil_div(E, 64));
+  router_gemm_kernel<<<grid, 256, 0, stream>>>(x, ldx, wsplit, T, H, E, logits);
   return hipGetLastError();
 }
 
