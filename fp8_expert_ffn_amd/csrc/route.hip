@@ -19,9 +19,11 @@ namespace dmoe {
 // exact in FP32 and the three BF16 MFMAs sum exactly the products of the FP32
 // definition, with FP32 accumulation.
 //
-// Wave tile: (16*TT tokens) x (16*EE experts); the 4 waves of a workgroup split
-// H into quarters and their partial tiles are added in wave order through LDS
-// (fixed order: deterministic).
+// Wave tile: (16*TT tokens) x (16*EE experts); the NW waves of a workgroup split
+// H into NW ranges and their partial tiles are added in wave order through LDS
+// (fixed order: deterministic). Rows past T or E read row 0 (their sums are
+// never stored), so every load is unconditional and a wave can have the loads
+// of PF K-steps in flight at once (few tokens: the kernel waits on W_r reads).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void split3_bf16(const float (&w)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
 #pragma unroll
@@ -37,8 +39,8 @@ __device__ __forceinline__ void split3_bf16(const float (&w)[8], bf16x8& hi, bf1
   }
 }
 
-// NW waves split H into NW equal ranges (H % (32 NW) == 0).
-template <int TT, int EE, int NW>
+// NW waves split H into NW equal ranges (H % (32 NW PF) == 0).
+template <int TT, int EE, int NW, int PF>
 __global__ __launch_bounds__(64 * NW) void router_logits_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                 const float* __restrict__ w_r, int T, int H, int E,
                                                                 float* __restrict__ logits) {
@@ -53,20 +55,16 @@ __global__ __launch_bounds__(64 * NW) void router_logits_kernel(const uint16_t* 
   const int kbeg = wave * kq;
 
   const uint16_t* xrow[TT];
-  bool xok[TT];
 #pragma unroll
   for (int i = 0; i < TT; ++i) {
     const int t = t0 + 16 * i + r16;
-    xok[i] = t < T;
-    xrow[i] = x + (int64_t)(xok[i] ? t : 0) * ldx + kg;
+    xrow[i] = x + (int64_t)(t < T ? t : 0) * ldx + kg;
   }
   int64_t wrow[EE];
-  bool wok[EE];
 #pragma unroll
   for (int j = 0; j < EE; ++j) {
     const int e = e0 + 16 * j + r16;
-    wok[j] = e < E;
-    wrow[j] = (int64_t)(wok[j] ? e : 0) * H + kg;
+    wrow[j] = (int64_t)(e < E ? e : 0) * H + kg;
   }
 
   f32x4 acc[TT][EE];
@@ -75,32 +73,34 @@ __global__ __launch_bounds__(64 * NW) void router_logits_kernel(const uint16_t* 
 #pragma unroll
     for (int j = 0; j < EE; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k = kbeg; k < kbeg + kq; k += 32) {
-    bf16x8 a[TT];
+  for (int k0 = kbeg; k0 < kbeg + kq; k0 += 32 * PF) {
+    bf16x8 a[PF][TT];
+    f32x4 wv[PF][EE][2];
 #pragma unroll
-    for (int i = 0; i < TT; ++i) {
-      i32x4 v = xok[i] ? *reinterpret_cast<const i32x4*>(xrow[i] + k) : i32x4{0, 0, 0, 0};
-      a[i] = __builtin_bit_cast(bf16x8, v);
+    for (int pf = 0; pf < PF; ++pf) {
+      const int k = k0 + 32 * pf;
+#pragma unroll
+      for (int i = 0; i < TT; ++i) a[pf][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(xrow[i] + k));
+#pragma unroll
+      for (int j = 0; j < EE; ++j) {
+        wv[pf][j][0] = *reinterpret_cast<const f32x4*>(w_r + wrow[j] + k);
+        wv[pf][j][1] = *reinterpret_cast<const f32x4*>(w_r + wrow[j] + k + 4);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < EE; ++j) {
-      float wv[8];
-      if (wok[j]) {
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(w_r + wrow[j] + k);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(w_r + wrow[j] + k + 4);
-        wv[0] = w0[0]; wv[1] = w0[1]; wv[2] = w0[2]; wv[3] = w0[3];
-        wv[4] = w1[0]; wv[5] = w1[1]; wv[6] = w1[2]; wv[7] = w1[3];
-      } else {
+    for (int pf = 0; pf < PF; ++pf) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) wv[q] = 0.f;
-      }
-      bf16x8 hi, mid, lo;
-      split3_bf16(wv, hi, mid, lo);
+      for (int j = 0; j < EE; ++j) {
+        const float w[8] = {wv[pf][j][0][0], wv[pf][j][0][1], wv[pf][j][0][2], wv[pf][j][0][3],
+                            wv[pf][j][1][0], wv[pf][j][1][1], wv[pf][j][1][2], wv[pf][j][1][3]};
+        bf16x8 hi, mid, lo;
+        split3_bf16(w, hi, mid, lo);
 #pragma unroll
-      for (int i = 0; i < TT; ++i) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], hi, acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], mid, acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], lo, acc[i][j], 0, 0, 0);
+        for (int i = 0; i < TT; ++i) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[pf][i], hi, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[pf][i], mid, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[pf][i], lo, acc[i][j], 0, 0, 0);
+        }
       }
     }
   }
@@ -133,15 +133,17 @@ __global__ __launch_bounds__(64 * NW) void router_logits_kernel(const uint16_t* 
 hipError_t launch_router_logits(const uint16_t* x, int64_t ldx, const float* w_r, int T, int H, int E,
                                 float* logits, hipStream_t stream) {
   if (T <= 256) {
-    // few tokens: the weight read dominates; 16 waves per workgroup keep more of it in flight
+    // few tokens: the weight read dominates; 16 waves per workgroup, each with up to 5 K-steps of loads in flight
     dim3 grid((T + 15) / 16, (E + 15) / 16);
-    if (H % 512 == 0)
-      router_logits_kernel<1, 1, 16><<<grid, 1024, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
+    if (H % 2560 == 0)
+      router_logits_kernel<1, 1, 16, 5><<<grid, 1024, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
+    else if (H % 512 == 0)
+      router_logits_kernel<1, 1, 16, 1><<<grid, 1024, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
     else
-      router_logits_kernel<1, 1, 4><<<grid, 256, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
+      router_logits_kernel<1, 1, 4, 1><<<grid, 256, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
   } else {
     dim3 grid((T + 63) / 64, (E + 63) / 64);
-    router_logits_kernel<4, 4, 4><<<grid, 256, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
+    router_logits_kernel<4, 4, 4, 1><<<grid, 256, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
   }
   return hipGetLastError();
 }
