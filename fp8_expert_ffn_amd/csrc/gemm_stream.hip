@@ -81,6 +81,11 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
     srcB[i] = base + (int64_t)(n0 + row % CW) * p.ldw_b + 16 * swz(row, lane & 7);
   }
 
+  // A routed expert whose rows fit one pass reads its weights exactly once:
+  // stream them with the non-temporal policy. The shared expert's row chunks
+  // and multi-pass experts read the same weights again and keep the default.
+  const bool read_once = (int)blockIdx.y < p.E_loc && row_end - row_beg <= AR;
+
   for (int m0 = row_beg; m0 < row_end; m0 += AR) {
     // A copy of wave w: rows (AR / 4) w .. + AR / 4 - 1 (R = 1: lanes 0..31)
     const int arow_l = (AR / 4) * wave + (lane >> 3);
@@ -97,7 +102,10 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
       uint8_t* st = ring[s % NS];
       const int64_t off = (int64_t)s * 128;
 #pragma unroll
-      for (int i = 0; i < WR / 32; ++i) lds_copy16(srcB[i] + off, st + (8 * (4 * i + wave)) * 128);
+      for (int i = 0; i < WR / 32; ++i) {
+        if (read_once) lds_copy16_nt(srcB[i] + off, st + (8 * (4 * i + wave)) * 128);
+        else lds_copy16(srcB[i] + off, st + (8 * (4 * i + wave)) * 128);
+      }
       if (a_lane) lds_copy16(srcA + off, st + (WR + (AR / 4) * wave) * 128);
       if (kFP8 && lane < 8) lds_copy4(srcS + s, &lsa[s % NS][8 * wave]);
     };
