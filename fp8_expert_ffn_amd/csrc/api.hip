@@ -115,7 +115,8 @@ dmoe_status dmoe_route_grouped(const float* logits, int32_t T, int32_t E, int32_
   REQ_PTR(topk_ids, "topk_ids");
   REQ_PTR(topk_w, "topk_w");
   const int g = n_group <= 1 ? 1 : n_group;
-  return hip_status(launch_route(logits, T, E, K, g, topk_group <= 0 ? g : topk_group, renormalize != 0,
+  return hip_status(launch_route(LogitSrc{logits, 1, 0, nullptr}, T, E, K, g, topk_group <= 0 ? g : topk_group,
+                                 renormalize != 0,
                                  routed_scaling_factor, topk_ids, topk_w, stream),
                     "route launch");
 }
@@ -137,7 +138,8 @@ dmoe_status dmoe_route_sigmoid(const float* logits, const float* score_bias, int
   REQ_PTR(topk_ids, "topk_ids");
   REQ_PTR(topk_w, "topk_w");
   const int g = n_group <= 1 ? 1 : n_group;
-  return hip_status(launch_route_sigmoid(logits, score_bias, T, E, K, g, topk_group <= 0 ? g : topk_group,
+  return hip_status(launch_route_sigmoid(LogitSrc{logits, 1, 0, nullptr}, score_bias, T, E, K, g,
+                                         topk_group <= 0 ? g : topk_group,
                                          renormalize != 0, routed_scaling_factor, topk_ids, topk_w, stream),
                     "route launch");
 }
@@ -402,7 +404,7 @@ dmoe_status dmoe_combine(const uint16_t* o, int64_t ldo, const int32_t* token_ro
 // ---------------------------------------------------------------------------
 namespace {
 enum { W_OFFSETS, W_ROW_TOKEN, W_ROW_SLOT, W_TOKEN_ROW, W_XQ, W_XS, W_H, W_HQ, W_HS, W_O, W_S, W_PERM, W_GEMM,
-       W_SHARED, W_RSPLIT, W_COUNT };
+       W_SHARED, W_RSPLIT, W_RPART, W_COUNT };
 
 struct FwdLayout {
   int64_t off[W_COUNT];
@@ -415,6 +417,12 @@ bool fuse_shared(const dmoe_layer_desc* d) { return d->T_s > 0 && d->F_s > 0 && 
 
 // Many tokens: the router runs as a tiled GEMM over W_r split once into BF16 parts.
 bool router_tiled(const dmoe_layer_desc* d) { return !d->logits_given && d->T > 256; }
+
+// Few tokens: the router's K ranges run as separate workgroups and leave
+// partial planes that the route launch adds; 1 = logits written directly.
+int router_planes(const dmoe_layer_desc* d) {
+  return (d->logits_given || router_tiled(d)) ? 1 : router_nparts(d->T, d->H);
+}
 
 FwdLayout fwd_layout(const dmoe_layer_desc* d) {
   FwdLayout L;
@@ -440,6 +448,7 @@ FwdLayout fwd_layout(const dmoe_layer_desc* d) {
       (int64_t)gemm_ws_bytes((int)mcap, d->E_loc, fused ? d->T_s : 0),
       (shared && !fused) ? shared_layout(d->dtype, d->T_s, d->H, d->F_s).total : -1,
       router_tiled(d) ? (int64_t)router_split_bytes(d->E, d->H) : -1,
+      router_planes(d) > 1 ? (int64_t)router_planes(d) * d->T * d->E * 4 : -1,
   };
   int64_t at = 0;
   for (int i = 0; i < W_COUNT; ++i) {
@@ -560,23 +569,32 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
   } while (0)
 
   STEP(mark(), "event");
-  if (!d->logits_given)
-    STEP(router_tiled(d) ? launch_router_logits_split(p->x, p->ldx, p->w_router, d->T, d->H, d->E,
-                                                      reinterpret_cast<uint16_t*>(at(W_RSPLIT)), p->logits, stream)
-                         : launch_router_logits(p->x, p->ldx, p->w_router, d->T, d->H, d->E, p->logits, stream),
-         "router_logits");
+  const int planes = router_planes(d);
+  float* rpart = planes > 1 ? reinterpret_cast<float*>(at(W_RPART)) : nullptr;
+  if (!d->logits_given) {
+    if (router_tiled(d))
+      STEP(launch_router_logits_split(p->x, p->ldx, p->w_router, d->T, d->H, d->E,
+                                      reinterpret_cast<uint16_t*>(at(W_RSPLIT)), p->logits, stream),
+           "router_logits");
+    else if (planes > 1)
+      STEP(launch_router_logits_parts(p->x, p->ldx, p->w_router, d->T, d->H, d->E, rpart, stream), "router_logits");
+    else
+      STEP(launch_router_logits(p->x, p->ldx, p->w_router, d->T, d->H, d->E, p->logits, stream), "router_logits");
+  }
   STEP(mark(), "event");
   {
     const int g = d->n_group <= 1 ? 1 : d->n_group;
     const int tg = d->topk_group <= 0 ? g : d->topk_group;
     const float sc = d->routed_scaling_factor == 0.f ? 1.f : d->routed_scaling_factor;
+    // partial planes: the route launch adds them and stores the logits
+    const LogitSrc src = planes > 1 ? LogitSrc{rpart, planes, (int64_t)d->T * d->E, p->logits}
+                                    : LogitSrc{p->logits, 1, 0, nullptr};
     if (d->scoring == DMOE_SCORING_SIGMOID)
-      STEP(launch_route_sigmoid(p->logits, p->score_bias, d->T, d->E, d->K, g, tg, d->no_renormalize == 0, sc,
+      STEP(launch_route_sigmoid(src, p->score_bias, d->T, d->E, d->K, g, tg, d->no_renormalize == 0, sc,
                                 p->topk_ids, p->topk_w, stream),
            "route");
     else
-      STEP(launch_route(p->logits, d->T, d->E, d->K, g, tg, d->no_renormalize == 0, sc, p->topk_ids, p->topk_w,
-                        stream),
+      STEP(launch_route(src, d->T, d->E, d->K, g, tg, d->no_renormalize == 0, sc, p->topk_ids, p->topk_w, stream),
            "route");
   }
   STEP(mark(), "event");

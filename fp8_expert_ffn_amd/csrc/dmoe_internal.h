@@ -22,11 +22,25 @@ hipError_t launch_router_logits(const uint16_t* x, int64_t ldx, const float* w_r
 size_t router_split_bytes(int E, int H);
 hipError_t launch_router_logits_split(const uint16_t* x, int64_t ldx, const float* w_r, int T, int H, int E,
                                       uint16_t* wsplit, float* logits, hipStream_t stream);
+// Few tokens in dmoe_forward: router_nparts(T, H) > 1 partial planes [n][T][E]
+// over equal K ranges, which the route launches add in plane order.
+int router_nparts(int T, int H);
+hipError_t launch_router_logits_parts(const uint16_t* x, int64_t ldx, const float* w_r, int T, int H, int E,
+                                      float* parts, hipStream_t stream);
+// Where the route launches read the logits: n planes (1 or 4) of `plane`
+// floats from p (n = 1: the logits themselves); out != nullptr: the summed
+// logits are stored there.
+struct LogitSrc {
+  const float* p;
+  int n;
+  int64_t plane;
+  float* out;
+};
 // n_group <= 1: ungrouped; renormalize: divide by the selected experts' sum (norm_topk_prob)
-hipError_t launch_route(const float* logits, int T, int E, int K, int n_group, int topk_group, bool renormalize,
+hipError_t launch_route(const LogitSrc& logits, int T, int E, int K, int n_group, int topk_group, bool renormalize,
                         float scaling, int32_t* ids, float* w, hipStream_t stream);
 // sigmoid scoring; bias: per-expert selection bias or nullptr
-hipError_t launch_route_sigmoid(const float* logits, const float* bias, int T, int E, int K, int n_group,
+hipError_t launch_route_sigmoid(const LogitSrc& logits, const float* bias, int T, int E, int K, int n_group,
                                 int topk_group, bool renormalize, float scaling, int32_t* ids, float* w,
                                 hipStream_t stream);
 

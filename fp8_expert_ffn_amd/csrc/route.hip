@@ -39,7 +39,10 @@ __device__ __forceinline__ void split3_bf16(const float (&w)[8], bf16x8& hi, bf1
   }
 }
 
-// NW waves split H into NW equal ranges (H % (32 NW PF) == 0).
+// NW waves split H into NW equal ranges (H % (32 NW PF) == 0). With
+// gridDim.z = KS > 1 workgroup z covers only the z-th of KS equal K ranges
+// (H % (32 NW PF KS) == 0) and stores its partial sums as plane z of `logits`
+// ([KS][T][E]); the planes are added in plane order by the route kernels.
 template <int TT, int EE, int NW, int PF>
 __global__ __launch_bounds__(64 * NW) void router_logits_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                 const float* __restrict__ w_r, int T, int H, int E,
@@ -51,8 +54,9 @@ __global__ __launch_bounds__(64 * NW) void router_logits_kernel(const uint16_t* 
   const int e0 = blockIdx.y * 16 * EE;
   const int r16 = lane & 15;
   const int kg = (lane >> 4) * 8;
-  const int kq = H / NW;
-  const int kbeg = wave * kq;
+  const int kq = H / (NW * (int)gridDim.z);
+  const int kbeg = (int)blockIdx.z * (H / (int)gridDim.z) + wave * kq;
+  logits += (int64_t)blockIdx.z * T * E;
 
   const uint16_t* xrow[TT];
 #pragma unroll
@@ -145,6 +149,23 @@ hipError_t launch_router_logits(const uint16_t* x, int64_t ldx, const float* w_r
     dim3 grid((T + 63) / 64, (E + 63) / 64);
     router_logits_kernel<4, 4, 4, 1><<<grid, 256, 0, stream>>>(x, ldx, w_r, T, H, E, logits);
   }
+  return hipGetLastError();
+}
+
+int router_nparts(int T, int H) { return (T <= 256 && H % 1024 == 0) ? 4 : 1; }
+
+hipError_t launch_router_logits_parts(const uint16_t* x, int64_t ldx, const float* w_r, int T, int H, int E,
+                                      float* parts, hipStream_t stream) {
+  // Few tokens: 4 K ranges x (16-token, 16-expert) tiles give 4x the
+  // workgroups of the single-plane launch, each with 8 waves whose loads of
+  // up to 5 K-steps are all in flight at once.
+  const int ks = router_nparts(T, H);
+  if (ks != 4) return hipErrorInvalidValue;
+  dim3 grid((T + 15) / 16, (E + 15) / 16, ks);
+  if (H % 5120 == 0)
+    router_logits_kernel<1, 1, 8, 5><<<grid, 512, 0, stream>>>(x, ldx, w_r, T, H, E, parts);
+  else
+    router_logits_kernel<1, 1, 8, 1><<<grid, 512, 0, stream>>>(x, ldx, w_r, T, H, E, parts);
   return hipGetLastError();
 }
 
@@ -365,6 +386,20 @@ __device__ __forceinline__ void keep_best_groups(uint64_t (&key)[VPL], int lane,
   }
 }
 
+// The logit of (t, e): element t * E + e of plane 0, plus that of planes
+// 1 .. NP - 1 in plane order (NP > 1: partial sums of the router's K ranges).
+// NP is a compile-time count so that the NP loads are issued together.
+template <int NP>
+__device__ __forceinline__ float logit_at(const LogitSrc& s, int64_t i) {
+  float v[NP];
+#pragma unroll
+  for (int c = 0; c < NP; ++c) v[c] = s.p[c * s.plane + i];
+  float r = v[0];
+#pragma unroll
+  for (int c = 1; c < NP; ++c) r += v[c];
+  return r;
+}
+
 // Routing options (Dots3NoteTextConfig n_group, topk_group, norm_topk_prob,
 // routed_scaling_factor).
 struct RouteOpts {
@@ -373,19 +408,23 @@ struct RouteOpts {
   float scaling;
 };
 
-template <int VPL>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int K,
-                                                    RouteOpts opt, int32_t* __restrict__ ids,
-                                                    float* __restrict__ wts) {
+template <int VPL, int NP>
+__global__ __launch_bounds__(256) void route_kernel(const LogitSrc src, int T, int E, int K, RouteOpts opt,
+                                                    int32_t* __restrict__ ids, float* __restrict__ wts) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + (int64_t)t * E;
+  const int64_t row = (int64_t)t * E;
   uint64_t key[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
-    key[i] = e < E ? route_key(row[e], (uint32_t)e) : 0ull;  // 0 sorts below every finite key
+    key[i] = 0ull;  // 0 sorts below every finite key
+    if (e < E) {
+      const float v = logit_at<NP>(src, row + e);
+      if (src.out) src.out[row + e] = v;
+      key[i] = route_key(v, (uint32_t)e);
+    }
   }
   if (opt.n_group > 1) keep_best_groups(key, lane, E, opt.n_group, opt.topk_group);
   uint64_t mine = 0;
@@ -413,7 +452,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int e = lane + 64 * i;
-      if (e < E) part += exp((double)row[e] - (double)vmax);
+      if (e < E) part += exp((double)logit_at<NP>(src, row + e) - (double)vmax);
     }
     sum = wave_sum_f64(part);
   }
@@ -432,21 +471,22 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float sigmoid_score(float l) { return (float)(1.0 / (1.0 + exp(-(double)l))); }
 
-template <int VPL>
-__global__ __launch_bounds__(256) void route_sigmoid_kernel(const float* __restrict__ logits,
-                                                            const float* __restrict__ bias, int T, int E, int K,
-                                                            RouteOpts opt, int32_t* __restrict__ ids,
-                                                            float* __restrict__ wts) {
+template <int VPL, int NP>
+__global__ __launch_bounds__(256) void route_sigmoid_kernel(const LogitSrc src, const float* __restrict__ bias,
+                                                            int T, int E, int K, RouteOpts opt,
+                                                            int32_t* __restrict__ ids, float* __restrict__ wts) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + (int64_t)t * E;
+  const int64_t row = (int64_t)t * E;
   uint64_t key[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      const float b = sigmoid_score(row[e]) + (bias ? bias[e] : 0.f);
+      const float l = logit_at<NP>(src, row + e);
+      if (src.out) src.out[row + e] = l;
+      const float b = sigmoid_score(l) + (bias ? bias[e] : 0.f);
       key[i] = route_key(b, (uint32_t)e);
     } else {
       key[i] = 0ull;
@@ -501,7 +541,7 @@ __global__ __launch_bounds__(256) void route_sigmoid_kernel(const float* __restr
     if (lane == k) mine = best;
   }
   const int e = (int)(~(uint32_t)mine);
-  const double s = lane < K ? (double)sigmoid_score(row[e]) : 0.0;
+  const double s = lane < K ? (double)sigmoid_score(logit_at<NP>(src, row + e)) : 0.0;
   const double sum = opt.renormalize ? wave_sum_f64(s) : 1.0;
   if (lane < K) {
     ids[(int64_t)t * K + lane] = e;
@@ -509,30 +549,42 @@ __global__ __launch_bounds__(256) void route_sigmoid_kernel(const float* __restr
   }
 }
 
-hipError_t launch_route_sigmoid(const float* logits, const float* bias, int T, int E, int K, int n_group,
+hipError_t launch_route_sigmoid(const LogitSrc& logits, const float* bias, int T, int E, int K, int n_group,
                                 int topk_group, bool renormalize, float scaling, int32_t* ids, float* w,
                                 hipStream_t stream) {
   const dim3 grid((T + 3) / 4);
   const int vpl = (E + 63) / 64;
   const RouteOpts opt{n_group, topk_group, renormalize, scaling};
-  if (vpl <= 1) route_sigmoid_kernel<1><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
-  else if (vpl <= 2) route_sigmoid_kernel<2><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
-  else if (vpl <= 4) route_sigmoid_kernel<4><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
-  else if (vpl <= 8) route_sigmoid_kernel<8><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
-  else route_sigmoid_kernel<16><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
+  auto go = [&](auto npc) {
+    constexpr int NP = decltype(npc)::value;
+    if (vpl <= 1) route_sigmoid_kernel<1, NP><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
+    else if (vpl <= 2) route_sigmoid_kernel<2, NP><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
+    else if (vpl <= 4) route_sigmoid_kernel<4, NP><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
+    else if (vpl <= 8) route_sigmoid_kernel<8, NP><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
+    else route_sigmoid_kernel<16, NP><<<grid, 256, 0, stream>>>(logits, bias, T, E, K, opt, ids, w);
+  };
+  if (logits.n == 1) go(std::integral_constant<int, 1>{});
+  else if (logits.n == 4) go(std::integral_constant<int, 4>{});
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_route(const float* logits, int T, int E, int K, int n_group, int topk_group, bool renormalize,
+hipError_t launch_route(const LogitSrc& logits, int T, int E, int K, int n_group, int topk_group, bool renormalize,
                         float scaling, int32_t* ids, float* w, hipStream_t stream) {
   const dim3 grid((T + 3) / 4);
   const int vpl = (E + 63) / 64;
   const RouteOpts opt{n_group, topk_group, renormalize, scaling};
-  if (vpl <= 1) route_kernel<1><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
-  else if (vpl <= 2) route_kernel<2><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
-  else if (vpl <= 4) route_kernel<4><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
-  else if (vpl <= 8) route_kernel<8><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
-  else route_kernel<16><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
+  auto go = [&](auto npc) {
+    constexpr int NP = decltype(npc)::value;
+    if (vpl <= 1) route_kernel<1, NP><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
+    else if (vpl <= 2) route_kernel<2, NP><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
+    else if (vpl <= 4) route_kernel<4, NP><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
+    else if (vpl <= 8) route_kernel<8, NP><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
+    else route_kernel<16, NP><<<grid, 256, 0, stream>>>(logits, T, E, K, opt, ids, w);
+  };
+  if (logits.n == 1) go(std::integral_constant<int, 1>{});
+  else if (logits.n == 4) go(std::integral_constant<int, 4>{});
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
