@@ -60,6 +60,19 @@ CASES = {
                                        dtype="bf16", T_s=200, logits="router"),
     "mid_rows_nondiv_fp8": synth.LayerConfig("mid_rows_fp8", T=512, H=1024, F=1400, F_s=1400, E=64, E_loc=64, e0=0,
                                              K=8, dtype="fp8", T_s=512, logits="uniform"),
+    # few tokens with H % 1024 == 0: the router leaves four partial planes over K that the route kernel adds;
+    # ragged token and expert tiles, grouped selection without renormalisation (sum over all experts' logits),
+    # sigmoid scoring with a selection bias (one K-step per wave), and the largest T of that path
+    "planes_ragged_bf16": synth.LayerConfig("planes_ragged", T=50, H=1024, F=128, F_s=128, E=40, E_loc=40, e0=0,
+                                            K=4, dtype="bf16", T_s=50, logits="router"),
+    "planes_grouped_fp8": synth.LayerConfig("planes_grouped", T=200, H=1024, F=256, F_s=256, E=64, E_loc=64, e0=0,
+                                            K=8, dtype="fp8", T_s=200, logits="router", n_group=8, topk_group=3,
+                                            renormalize=False, scaling=2.5),
+    "planes_sigmoid_bf16": synth.LayerConfig("planes_sigmoid", T=96, H=2048, F=256, F_s=256, E=64, E_loc=64, e0=0,
+                                             K=6, dtype="bf16", T_s=96, logits="router", n_group=8, topk_group=4,
+                                             scoring="sigmoid", scaling=1.5),
+    "planes_t256_bf16": synth.LayerConfig("planes_t256", T=256, H=1024, F=128, F_s=0, E=32, E_loc=32, e0=0, K=4,
+                                          dtype="bf16", T_s=0, logits="router"),
 }
 
 
