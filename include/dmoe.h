@@ -315,7 +315,9 @@ dmoe_status dmoe_forward(const dmoe_layer_desc* desc, const dmoe_layer_ptrs* ptr
  * profiler or benchmark can time each stage on the stream it runs on.
  * stage_events: host array of DMOE_STAGES + 1 hipEvent_t; event i is recorded
  * before stage i and event DMOE_STAGES after the last one. Stages, in order:
- * 0 router logits (empty when logits are given), 1 route, 2 permute and tile
+ * 0 router logits (empty when logits are given; with T <= 256 and
+ * H % 1024 == 0 it leaves four partial sums over K in the workspace, which
+ * stage 1 adds and stores in ptrs.logits), 1 route, 2 permute and tile
  * schedule, 3 quantise x (FP8), 4 gate/up + SwiGLU, 5 quantise h (FP8),
  * 6 down, 7 shared expert, 8 combine. A NULL entry is skipped (each recorded
  * event is a stream marker that costs a few microseconds of queue time).
