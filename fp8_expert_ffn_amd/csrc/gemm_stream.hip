@@ -47,7 +47,8 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
   constexpr int AR = 16 * R;              // A rows per pass
   constexpr int kRows = WR + AR;
   constexpr int NS = kFP8 ? kRingFP8 : kRingBF16;
-  constexpr int kCopies = WR / 32 + 1 + (kFP8 ? 1 : 0);  // direct copies per wave per stage
+  constexpr int kCopiesA = 1 + (kFP8 ? 1 : 0);  // A-row (+ scale) copies per wave per stage
+  constexpr int kCopies = WR / 32 + kCopiesA;    // direct copies per wave per stage
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][kRows * 128];
   __shared__ __attribute__((aligned(256))) float lsa[NS][32];
   __shared__ float lsw[2][kMaxSlices];
@@ -86,7 +87,23 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
   // and multi-pass experts read the same weights again and keep the default.
   const bool read_once = (int)blockIdx.y < p.E_loc && row_end - row_beg <= AR;
 
+  const int S0 = min(NS - 1, S);  // stages issued ahead of the ring loop
   for (int m0 = row_beg; m0 < row_end; m0 += AR) {
+    // Weight copies of stage s; they need no row index.
+    auto issue_w = [&](int s) {
+      uint8_t* st = ring[s % NS];
+      const int64_t off = (int64_t)s * 128;
+#pragma unroll
+      for (int i = 0; i < WR / 32; ++i) {
+        if (read_once) lds_copy16_nt(srcB[i] + off, st + (8 * (4 * i + wave)) * 128);
+        else lds_copy16(srcB[i] + off, st + (8 * (4 * i + wave)) * 128);
+      }
+    };
+    // The first stages' weight copies go out before the A rows' token indices
+    // are loaded, so the ring fill waits for one memory round trip instead of
+    // two in a row (token index, then weights).
+    for (int s = 0; s < S0; ++s) issue_w(s);
+
     // A copy of wave w: rows (AR / 4) w .. + AR / 4 - 1 (R = 1: lanes 0..31)
     const int arow_l = (AR / 4) * wave + (lane >> 3);
     const bool a_lane = lane < 2 * AR;  // 8 lanes per row, AR / 4 rows per wave
@@ -98,14 +115,10 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
     const int sm = m0 + srow_l;
     const float* srcS = kFP8 ? p.a_scales + a_row(p, gv, (lane < 8 && sm < row_end) ? sm : m0) * p.ldas : nullptr;
 
-    auto issue = [&](int s) {
+    // A-row and activation-scale copies of stage s (kCopiesA per wave)
+    auto issue_a = [&](int s) {
       uint8_t* st = ring[s % NS];
       const int64_t off = (int64_t)s * 128;
-#pragma unroll
-      for (int i = 0; i < WR / 32; ++i) {
-        if (read_once) lds_copy16_nt(srcB[i] + off, st + (8 * (4 * i + wave)) * 128);
-        else lds_copy16(srcB[i] + off, st + (8 * (4 * i + wave)) * 128);
-      }
       if (a_lane) lds_copy16(srcA + off, st + (WR + (AR / 4) * wave) * 128);
       if (kFP8 && lane < 8) lds_copy4(srcS + s, &lsa[s % NS][8 * wave]);
     };
@@ -187,11 +200,18 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
     };
 
     // ---- NS-stage ring: stage s lives in buffer s % NS ----
-    for (int s = 0; s < NS - 1 && s < S; ++s) issue(s);
+    // Issue order per wave: W(0 .. S0-1), A(0 .. S0-1), then W(s) A(s) for
+    // s = S0, S0+1, ... So stage s < NS - 1 is complete once at most the
+    // A copies of stages s+1 .. NS-2 and the s+1 stages issued in the loop
+    // are in flight; (NS - 2) kCopiesA + kCopies is the smallest of those
+    // counts (s = 0), conservative for 0 < s < NS - 1.
+    for (int s = 0; s < S0; ++s) issue_a(s);
     for (int s = 0; s < S; ++s) {
       if (s + NS - 1 < S) {
-        issue(s + NS - 1);
-        wait_vmcnt<kCopies * (NS - 1)>();  // stage s complete: at most the NS-1 younger stages in flight
+        issue_w(s + NS - 1);
+        issue_a(s + NS - 1);
+        if (s < NS - 1) wait_vmcnt<(NS - 2) * kCopiesA + kCopies>();
+        else wait_vmcnt<kCopies * (NS - 1)>();  // at most the NS-1 younger stages in flight
       } else {
         wait_vmcnt<0>();
       }
