@@ -23,7 +23,7 @@ namespace dmoe {
 // the group's (up to 16 R) A rows and of their FP8 scales moves global -> LDS
 // with direct loads (each instruction covers 8 whole 128-byte lines) through a
 // ring of kRingBF16 or kRingFP8 stages (a 128-byte BF16 stage holds half the K
-// of an FP8 one). Grid: (N_pad / CW, E_loc + chunks).
+// of an FP8 one). Grid: (N_pad / CW, chunks + E_loc).
 // ---------------------------------------------------------------------------
 #ifndef DMOE_STAGE_RING_BF16
 #define DMOE_STAGE_RING_BF16 6
@@ -55,7 +55,13 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
   __shared__ f32x4 xup[kSplit ? 2 * R * 64 : 1];  // up accumulators of waves 2, 3
   asm volatile("" ::"v"(&ring[0][0]), "v"(&lsa[0][0]) : "memory");
 
-  const GroupView gv = group_view(p, blockIdx.y);
+  // Grid rows 0 .. chunks-1 are the extra group's row chunks, the rest the
+  // routed experts: the chunks, which all read the same weights, are dispatched
+  // first and together, and the last, partly filled round of workgroups is
+  // left to routed experts.
+  const int chunks = (int)gridDim.y - p.E_loc;
+  const int g = (int)blockIdx.y < chunks ? p.E_loc + (int)blockIdx.y : (int)blockIdx.y - chunks;
+  const GroupView gv = group_view(p, g);
   const int row_beg = gv.row_beg, row_end = gv.row_end;
   if (row_beg >= row_end) return;
   const int n0 = blockIdx.x * CW;
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(256) void gemm_stage_kernel(const TileArgs p, int n
   // A routed expert whose rows fit one pass reads its weights exactly once:
   // stream them with the non-temporal policy. The shared expert's row chunks
   // and multi-pass experts read the same weights again and keep the default.
-  const bool read_once = (int)blockIdx.y < p.E_loc && row_end - row_beg <= AR;
+  const bool read_once = g < p.E_loc && row_end - row_beg <= AR;
 
   const int S0 = min(NS - 1, S);  // stages issued ahead of the ring loop
   for (int m0 = row_beg; m0 < row_end; m0 += AR) {
