@@ -201,6 +201,37 @@ def sample_parity(cfg, results, y_gpu: np.ndarray, ids_gpu: np.ndarray) -> dict:
             "bound": "rel_l2 <= 5e-3; per element |dy| <= 2e-2 RMS + 1 BF16 ulp; <= 1% of elements over 2e-2 RMS"}
 
 
+def bit_exact(cfg, layer, d, ws, out, x_bits: np.ndarray) -> dict:
+    """Integer and byte results of the timed layer against the oracle at the full workload size: the top-K ids
+    from the GPU's own logits (the oracle routes the same FP32 logits), the routing weights (tolerance 1e-6), the
+    permutation tables of those ids and, for FP8, the codes and scales of x."""
+    import oracle
+    import synth
+    L = out["logits"].cpu().numpy()
+    ids_gpu = out["topk_ids"].cpu().numpy()
+    w_gpu = out["topk_w"].cpu().numpy()
+    ropts = dict(n_group=cfg.n_group, topk_group=cfg.topk_group or None, renormalize=cfg.renormalize,
+                 scaling=cfg.scaling)
+    if cfg.scoring == "sigmoid":
+        ids_or, w_or = oracle.route_sigmoid(L, cfg.K, bias=synth.score_bias(cfg), **ropts)
+    else:
+        ids_or, w_or = oracle.route(L, cfg.K, **ropts)
+    off, rt, rs, tr = oracle.permute(ids_gpu, cfg.e0, cfg.E_loc)
+    m = int(off[-1])
+    view = lambda name: layer.ws_view(d, ws, name).cpu().numpy()  # noqa: E731
+    rec = {"ids": bool(np.array_equal(ids_gpu, ids_or)),
+           "weights_max_abs_diff": float(np.max(np.abs(w_gpu.astype(np.float64) - w_or))),
+           "perm": bool(np.array_equal(view("offsets"), off) and np.array_equal(view("row_token")[:m], rt)
+                        and np.array_equal(view("row_slot")[:m], rs) and np.array_equal(view("token_row"), tr))}
+    if cfg.dtype == "fp8":
+        q, sc = oracle.quantize_act((x_bits.astype(np.uint32) << 16).view(np.float32))
+        rec["x_codes"] = bool(np.array_equal(view("x_codes"), q))
+        rec["x_scales"] = bool(np.array_equal(view("x_scales").view(np.uint32), sc.view(np.uint32)))
+    rec["pass"] = bool(rec["ids"] and rec["perm"] and rec["weights_max_abs_diff"] <= 1e-6
+                       and rec.get("x_codes", True) and rec.get("x_scales", True))
+    return rec
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,6 +411,7 @@ def main() -> int:
         y_gpu = out["y"].view(torch.int16).cpu().numpy().view(np.uint16)
         y_gpu = (y_gpu.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         result["parity_sample"] = sample_parity(cfg, results, y_gpu, out["topk_ids"].cpu().numpy())
+        result["bit_exact"] = bit_exact(cfg, layer, d, ws, out, x_bits)
     print(json.dumps(result), flush=True)
     return 0
 
