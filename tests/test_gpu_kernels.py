@@ -187,7 +187,9 @@ def _quant_case(x_bits: np.ndarray, cols=None):
     assert np.all(q[:, cols:] == 0)
 
 
-@pytest.mark.parametrize("rows,cols", [(2048, 5120), (33, 1400), (5, 40), (1, 128), (300, 1536)])
+# (2048, 5120) and (1009, 8312) take the launch with four slices per 16-lane group (>= 65536 slices); the latter
+# ends in a partly filled workgroup and a 120-wide last slice
+@pytest.mark.parametrize("rows,cols", [(2048, 5120), (1009, 8312), (33, 1400), (5, 40), (1, 128), (300, 1536)])
 def test_quant_act_workload_values(rows, cols):
     say(f"quant_act {rows}x{cols}")
     cfg = synth.LayerConfig("q", T=rows, H=cols, F=8, F_s=0, E=1, E_loc=1, e0=0, K=1, dtype="fp8", T_s=0,
