@@ -245,6 +245,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--graph", action="store_true",
                     help="also time the layer captured once in a HIP graph and replayed (decode-style serving)")
+    ap.add_argument("--tokens", type=int, default=0, metavar="T",
+                    help="run the workload's layer with T tokens instead of its own (the shared expert then takes "
+                         "min(T, its T_s) tokens, all of them when it took all before)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -265,6 +268,9 @@ def main() -> int:
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration, max(1, args.steps))
     cfg = synth.config(args.workload)
+    if args.tokens > 0:
+        t_s = args.tokens if cfg.T_s == cfg.T else min(cfg.T_s, args.tokens)
+        cfg = cfg.replace(name=f"{cfg.name}_T{args.tokens}", T=args.tokens, T_s=t_s)
     t0 = time.time()
     layer = build_layer(cfg, dev)
     x_bits = synth.x_bf16(cfg)

@@ -73,6 +73,17 @@ CASES = {
                                              scoring="sigmoid", scaling=1.5),
     "planes_t256_bf16": synth.LayerConfig("planes_t256", T=256, H=1024, F=128, F_s=0, E=32, E_loc=32, e0=0, K=4,
                                           dtype="bf16", T_s=0, logits="router"),
+    # few rows in all (the weight-streaming GEMMs): one token with 8 experts and the shared expert, three tokens
+    # on a non-divisible FFN, 17-32 rows per expert (two 16-row subtiles per pass), an EP share of 32 experts
+    # (e0 = 32) with untouched experts
+    "small_t1_bf16": synth.LayerConfig("small_t1", T=1, H=2048, F=512, F_s=512, E=64, E_loc=64, e0=0, K=8,
+                                       dtype="bf16", T_s=1, logits="router"),
+    "small_t3_nondiv_fp8": synth.LayerConfig("small_t3", T=3, H=1024, F=1400, F_s=1400, E=32, E_loc=32, e0=0,
+                                             K=4, dtype="fp8", T_s=3, logits="router"),
+    "stream_r2_fp8": synth.LayerConfig("stream_r2", T=40, H=512, F=256, F_s=256, E=16, E_loc=16, e0=0, K=8,
+                                       dtype="fp8", T_s=40, logits="uniform"),
+    "small_ep_bf16": synth.LayerConfig("small_ep", T=16, H=1024, F=256, F_s=256, E=256, E_loc=32, e0=32, K=8,
+                                       dtype="bf16", T_s=16, logits="zipf"),
 }
 
 
@@ -170,12 +181,16 @@ def test_zero_tokens_is_a_no_op():
     assert out["y"].shape == (0, cfg.H)
 
 
-def test_separate_entry_points_match_forward():
-    """route -> permute -> quant -> gateup -> quant -> down -> shared -> combine, one call at a time."""
+@pytest.mark.parametrize("name", ["nondiv_small_fp8", "prefill_small_fp8"])
+def test_separate_entry_points_match_forward(name):
+    """route -> permute -> quant -> gateup -> quant -> down -> shared -> combine, one call at a time, bit for bit
+    against dmoe_forward on the same logits (weight-streaming and tile GEMMs; the forward runs the shared expert
+    as an extra group of the routed launches, the entry point as a GEMM of its own)."""
     import fp8_expert_ffn_amd as dm
-    cfg, layer, x, x_bits, wr, given, ref = _run("nondiv_small_fp8")
-    full = layer.forward(x, cfg.T_s, logits=torch.from_numpy(given).to(DEV))["y"].clone()
-    ids, w = dm.dmoe_route(torch.from_numpy(given).to(DEV), cfg.K)
+    cfg, layer, x, x_bits, wr, given, ref = _run(name)
+    logits = torch.from_numpy(given if given is not None else ref.logits).to(DEV)
+    full = layer.forward(x, cfg.T_s, logits=logits)["y"].clone()
+    ids, w = dm.dmoe_route(logits, cfg.K)
     off, rt, rs, tr = dm.dmoe_permute(ids, cfg.e0, cfg.E_loc)
     xq, xs = dm.dmoe_quant_act(x)
     mcap = cfg.T * cfg.K
