@@ -213,6 +213,7 @@ def router_logits(x: np.ndarray, w_r: np.ndarray) -> np.ndarray:
 
     Router output shape (batch*seq, num_experts): Transformers docs "Dots3Note",
     ``router_logits`` output entry; FP32 routing: PR #47844 implementation list.
+    parity pinned (brute force, special weights).
     """
     return (np.asarray(x, dtype=np.float64) @ np.asarray(w_r, dtype=np.float64).T).astype(np.float32)
 

@@ -278,3 +278,42 @@ def test_sigmoid_route_without_bias_is_monotone_in_logits():
     s = oracle.sigmoid_scores(L)
     distinct = np.array([np.unique(np.sort(s[t])[::-1][:9]).size == 9 for t in range(L.shape[0])])
     np.testing.assert_array_equal(ids_s[distinct], ids_m[distinct])
+
+
+# --------------------------------------------------------------------------- router logits
+
+def _bf16_values(rng, shape):
+    """Random finite BF16 values (as float64): float32 draws with the low 16 bits cleared."""
+    v = rng.standard_normal(shape).astype(np.float32)
+    return (v.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+
+
+def test_router_logits_brute_force_sum():
+    """Every logit is the FP32 rounding of the exact dot product: each BF16 x FP32 product is exact in float64,
+    math.fsum adds them with one rounding, and the float32 cast rounds once more."""
+    import math
+    rng = np.random.default_rng(11)
+    T, E, H = 6, 5, 96
+    x = _bf16_values(rng, (T, H))
+    w = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    got = oracle.router_logits(x, w)
+    assert got.dtype == np.float32 and got.shape == (T, E)
+    want = np.array([[np.float32(math.fsum(float(x[t, h]) * float(w[e, h]) for h in range(H))) for e in range(E)]
+                     for t in range(T)], dtype=np.float32)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_router_logits_special_weights():
+    """One-hot router rows pick one hidden column of x exactly (so a transposed operand or a wrong index shows);
+    doubling W_r doubles every logit exactly; a negated row gives the negated logit."""
+    rng = np.random.default_rng(12)
+    T, H = 9, 40
+    x = _bf16_values(rng, (T, H))
+    cols = np.array([0, 7, 39, 13])
+    w = np.zeros((cols.size, H), np.float32)
+    w[np.arange(cols.size), cols] = 1.0
+    np.testing.assert_array_equal(oracle.router_logits(x, w), x[:, cols].astype(np.float32))
+    w2 = (rng.standard_normal((3, H)) * 0.05).astype(np.float32)
+    l2 = oracle.router_logits(x, w2)
+    np.testing.assert_array_equal(oracle.router_logits(x, 2 * w2), 2 * l2)
+    np.testing.assert_array_equal(oracle.router_logits(x, -w2), -l2)
