@@ -7,9 +7,11 @@
 A step is one dmoe_forward over one batch of synthetic input: router logits
 (or given logits) -> route -> permute -> [quantise x] -> gate/up + SwiGLU ->
 [quantise h] -> down -> shared expert -> combine. Inputs and weights are
-resident in HBM before the timed region. The default workload is the BF16
-decode layer at full dots3-note shape (T=64 tokens, hidden 5120, 256 routed +
-1 shared experts, top-8, expert FFN 1536). Prints one JSON line.
+resident in HBM before the timed region. The default workload is the FP8
+prefill chunk at full dots3-note shape (T=8192 tokens, hidden 5120, 256 routed
++ 1 shared experts, top-8, expert FFN 1536, E4M3 weights with 128x128 block
+scales and dynamic 1x128 activation scales); --workload 1 is the BF16 decode
+layer (T=64). Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -178,27 +180,27 @@ def cpu_baseline(cfg, x_bits, wr, given, seconds: float):
 
 def sample_parity(cfg, results, y_gpu: np.ndarray, ids_gpu: np.ndarray) -> dict:
     """GPU output of the timed layer against the oracle on the cpu_baseline's sampled tokens. Tokens whose top-K
-    set differs (router near-ties between the GPU's FP32 logits and the oracle's) are left out and counted."""
+    set differs (router near-ties between the GPU's FP32 logits and the oracle's) are left out and counted.
+    Bound: relative L2 <= 5e-3 against the oracle's BF16 y, and every element within 2e-2 RMS plus half a BF16
+    ulp (the GPU's own final rounding) of the oracle's unrounded float64 sum."""
     tok = np.concatenate([r.tokens for r in results])
     y_or = np.concatenate([r.y for r in results])
+    y_sum = np.concatenate([r.y_sum for r in results])
     ids_or = np.concatenate([r.ids for r in results])
     same = np.all(np.sort(ids_gpu[tok], 1) == np.sort(ids_or, 1), axis=1)
-    yg, yo = y_gpu[tok][same], y_or[same]
+    yg, yo, ys = y_gpu[tok][same], y_or[same], y_sum[same]
     if yo.size == 0:
         return {"tokens": 0}
     rms = float(np.sqrt(np.mean(yo ** 2)))
-    err = np.abs(yg - yo)
-    # both sides are BF16 roundings, so one element may differ by one BF16 ulp of itself on top of 2e-2 RMS
-    a = np.abs(yo)
-    ulp = np.where(a > 0, np.ldexp(1.0, np.maximum(np.frexp(a)[1] - 8, -133)), 0.0)
-    worst = float(np.max(err / np.maximum(2e-2 * rms + ulp, 1e-300)))
+    a = np.maximum(np.abs(yg), np.abs(ys))
+    half_ulp = np.where(a > 0, np.ldexp(1.0, np.maximum(np.frexp(a)[1] - 9, -134)), 0.0)
+    worst = float(np.max(np.abs(yg - ys) / np.maximum(2e-2 * rms + half_ulp, 1e-300)))
     rel = float(np.linalg.norm(yg - yo) / max(np.linalg.norm(yo), 1e-300))
-    over = float(np.mean(err > 2e-2 * rms))
     return {"tokens": int(same.sum()), "routing_near_ties_skipped": int((~same).sum()),
-            "rel_l2": rel, "max_abs_over_rms": float(err.max() / max(rms, 1e-300)),
-            "frac_over_2e-2_rms": over, "max_err_over_bound": worst,
-            "pass": bool(rel <= 5e-3 and worst <= 1.0 and over <= 1e-2),
-            "bound": "rel_l2 <= 5e-3; per element |dy| <= 2e-2 RMS + 1 BF16 ulp; <= 1% of elements over 2e-2 RMS"}
+            "rel_l2": rel, "max_abs_over_rms": float(np.abs(yg - yo).max() / max(rms, 1e-300)),
+            "max_err_over_bound": worst, "pass": bool(rel <= 5e-3 and worst <= 1.0),
+            "bound": "rel_l2 <= 5e-3; every element |y - y_sum| <= 2e-2 RMS + ulp_bf16/2 (y_sum: the oracle's "
+                     "unrounded combine sum)"}
 
 
 def bit_exact(cfg, layer, d, ws, out, x_bits: np.ndarray) -> dict:
@@ -237,7 +239,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1, help="workload index (0 tiny, 1 decode, 2 prefill, "
+    ap.add_argument("--workload", type=int, default=2, help="workload index (0 tiny, 1 decode, 2 prefill, "
                                                                 "3 EP share, 4 non-divisible, 5 vision BF16, "
                                                                 "6 vision FP8, 7 dense FFN FP8, "
                                                                 "8/9 speculative verify batch BF16/FP8)")
@@ -363,14 +365,17 @@ def main() -> int:
     gu_sec = gu_ms / 1e3
     gu_time_hbm = acc["gu_bytes"] / (PEAK_HBM_GBPS * 1e9)
     gu_time_mfma = acc["gu_flops"] / (PEAK_TFLOPS[cfg.dtype] * 1e12)
+    ach_hbm = acc["gu_bytes"] / gu_sec / 1e9
+    ach_mfma = acc["gu_flops"] / gu_sec / 1e12
+    hbm_side = {"achieved": round(ach_hbm, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(ach_hbm / PEAK_HBM_GBPS, 4)}
+    mfma_side = {"achieved": round(ach_mfma, 1), "peak": PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s",
+                 "frac": round(ach_mfma / PEAK_TFLOPS[cfg.dtype], 4)}
+    # the binding resource at peak rates decides `bound`; the other side is reported next to it
     if gu_time_hbm >= gu_time_mfma:
-        achieved = acc["gu_bytes"] / gu_sec / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None}
+        roof = {"bound": "hbm", **hbm_side, "traffic": None, "other_roof": {"bound": "mfma", **mfma_side}}
     else:
-        achieved = acc["gu_flops"] / gu_sec / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_TFLOPS[cfg.dtype], 4), "traffic": None}
+        roof = {"bound": "mfma", **mfma_side, "traffic": None, "other_roof": {"bound": "hbm", **hbm_side}}
     stream_k = uses_stream_kernel(cfg)
     kname = f"{'gemm_stage_kernel' if stream_k else 'gemm_tile_kernel'}<{cfg.dtype}, gate/up>"
     roof["kernel"] = kname + (" (routed experts + shared expert as an extra group)" if shared_fused(cfg)

@@ -1,7 +1,7 @@
 // Grouped expert GEMMs: gate/up with fused SwiGLU, and down.
 //
 // Expert FFN: hidden_act silu over gate_proj/up_proj, then down_proj, no bias
-// (Transformers docs "Dots3Note", Dots3NoteTextConfig hidden_act, mlp_bias);
+// (Transformers documentation "Dots 3 Note Preview", Dots3NoteTextConfig hidden_act, mlp_bias);
 // 256 routed experts of width 1536 on hidden 5120 (model card
 // "dots-studio/dots3-note-prev", Model Overview table). FP8: E4M3 weights
 // with one FP32 scale per 128x128 block and dynamic activation scales per 1x128

@@ -2,8 +2,8 @@
 // through LDS.
 //
 // Same operation as the tile kernel in gemm.hip (gate/up with fused SwiGLU, or
-// down; FP8 block-scale promotion per 128-wide K slice; Transformers docs
-// "Dots3Note" and PR #47844), organised for the case where each expert sees a
+// down; FP8 block-scale promotion per 128-wide K slice; Transformers documentation
+// "Dots 3 Note Preview" and PR #47844), organised for the case where each expert sees a
 // handful of rows and the weights are read once from HBM.
 #include "gemm_common.h"
 

@@ -1,6 +1,6 @@
 // Expert-contiguous permutation of the routed (token, slot) pairs.
 //
-// The pages fix only the routing (Transformers docs "Dots3Note",
+// The pages fix only the routing (Transformers documentation "Dots 3 Note Preview",
 // Dots3NoteTextConfig num_experts_per_tok) and the EP8 deployment whose
 // grouped expert GEMMs need each expert's rows contiguous (SGLang cookbook
 // "Dots3-Note", Deployment: DP8 attention x TP8 x EP8, MoE runner). The order

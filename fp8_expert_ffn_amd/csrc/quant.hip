@@ -18,9 +18,12 @@ __device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, 
 // rounded division per element. Both operands are first scaled by the same
 // power of two so that the divisor lies in [1, 2); with the correctly rounded
 // reciprocal r of the divisor, q = v' r corrected once by the exact residual
-// v' - q s' (a fused multiply-add) is the correctly rounded quotient (the
-// classic reciprocal-and-correction division), and the sign of zero is
-// restored. The code chosen from it equals the code of the correctly rounded
+// v' - q s' (a fused multiply-add) is the quotient, and the sign of zero is
+// restored. This is the FMA correction step of Markstein's division
+// (P. Markstein, "Computation of elementary functions on the IBM RISC
+// System/6000 processor", IBM J. Res. Develop. 34(1), 1990): with r the
+// correctly rounded reciprocal, one step q + (v' - q s') r yields the
+// correctly rounded quotient except in rare cases that need a second step. The code chosen from it equals the code of the correctly rounded
 // f32(v / s) for every BF16 v and every scale s = f32(amax / 448) with
 // |v| <= amax (checked exhaustively on gfx950 for all BF16 amax); quotients
 // that differ in the last f32 bit are far below the smallest E4M3 subnormal.

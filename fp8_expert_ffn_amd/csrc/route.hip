@@ -2,7 +2,7 @@
 // group-limited) and softmax weights, one wavefront per token.
 //
 // FP32 routing: Transformers PR #47844, implementation list. Top-K with
-// renormalised weights: Transformers docs "Dots3Note", Dots3NoteTextConfig
+// renormalised weights: Transformers documentation "Dots 3 Note Preview", Dots3NoteTextConfig
 // (num_experts_per_tok, norm_topk_prob, routed_scaling_factor, n_group,
 // topk_group); the softmax scoring is the reading of the docs' "post-softmax"
 // router_logits entry.
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(256) void route_kernel(const LogitSrc src, int T, i
 
 // ---------------------------------------------------------------------------
 // Sigmoid scoring with a selection-only correction bias (the bias-balanced
-// routers the Transformers docs name in their aux_loss entry: DeepSeek-V3 and
+// routers the Transformers documentation "Dots 3 Note Preview" names in its aux_loss entry: DeepSeek-V3 and
 // its derivatives). s = f32(1 / (1 + exp(-l))) evaluated in double; the key
 // of expert e is f32(s + bias[e]); a group's score is f32(b1 + b2), its two
 // largest biased scores; weights come from the unbiased s.

@@ -3,7 +3,7 @@
  * an AMD Instinct MI355X (gfx950).
  *
  * The layer (model card "dots-studio/dots3-note-prev", Model Overview table;
- * Transformers docs "Dots3Note", Dots3NoteTextConfig parameters): 256 routed
+ * Transformers documentation "Dots 3 Note Preview", Dots3NoteTextConfig parameters): 256 routed
  * experts plus 1 shared expert, top-8 token-choice routing with renormalised
  * weights, hidden size 5120, per-expert SwiGLU FFN of width 1536, in BF16 or in
  * fine-grained FP8 (E4M3 weights with one FP32 scale per 128x128 block and
@@ -87,13 +87,14 @@ int32_t dmoe_abi_version(void);
 
 /*
  * Router logits, FP32: logits[t, e] = sum_h f32(x[t, h]) * w_r[e, h].
- * Follows: Transformers docs "Dots3Note", router_logits output of shape
- * (batch*seq, num_experts); FP32 routing (PR #47844, implementation list).
  * x: [T, ldx] BF16; w_r: [E, H] FP32 dense; logits: [T, E] FP32 dense.
  * The sum is accumulated in FP32 on matrix cores (each product exact); its
  * order differs from a sequential sum, so results agree with an exact sum to
  * FP32 accumulation error, not bit for bit.
  * Requires 1 <= E <= 1024, H % 128 == 0, T >= 0 (T == 0 is a no-op).
+ * Source: Transformers documentation "Dots 3 Note Preview", model outputs,
+ * router_logits entry (shape (batch*seq, num_experts)); Transformers PR #47844 "Add dots3-note Preview model support",
+ * implementation list (routing in FP32).
  */
 dmoe_status dmoe_router_logits(const uint16_t* x, int64_t ldx, const float* w_r, int32_t T, int32_t H,
                                int32_t E, float* logits, hipStream_t stream);
@@ -108,6 +109,11 @@ dmoe_status dmoe_router_logits(const uint16_t* x, int64_t ldx, const float* w_r,
  * logits: [T, E] FP32 (finite values; NaN behaviour is undefined);
  * topk_ids: [T, K] int32; topk_w: [T, K] FP32.
  * Requires 1 <= K <= E <= 1024, K <= 64.
+ * Source: Transformers documentation "Dots 3 Note Preview", Dots3NoteTextConfig
+ * num_experts_per_tok, norm_topk_prob, routed_scaling_factor, n_group,
+ * topk_group. The scoring function and the tie rule are not stated there:
+ * softmax (the conditional-generation forward calls its router output
+ * post-softmax) and lower index first are this library's readings.
  */
 dmoe_status dmoe_route(const float* logits, int32_t T, int32_t E, int32_t K, int32_t* topk_ids, float* topk_w,
                        hipStream_t stream);
@@ -128,6 +134,8 @@ dmoe_status dmoe_route(const float* logits, int32_t T, int32_t E, int32_t K, int
  * E % n_group == 0, 1 <= topk_group <= n_group, K <= topk_group * E / n_group,
  * and a positive finite routed_scaling_factor; otherwise as dmoe_route.
  * dmoe_route(...) is dmoe_route_grouped(..., 1, 1, 1, 1.0f, ...).
+ * Source: Transformers documentation "Dots 3 Note Preview", Dots3NoteTextConfig
+ * n_group, topk_group, norm_topk_prob, routed_scaling_factor.
  */
 dmoe_status dmoe_route_grouped(const float* logits, int32_t T, int32_t E, int32_t K, int32_t n_group,
                                int32_t topk_group, int32_t renormalize, float routed_scaling_factor,
@@ -135,7 +143,7 @@ dmoe_status dmoe_route_grouped(const float* logits, int32_t T, int32_t E, int32_
 
 /*
  * Sigmoid scoring with a selection-only correction bias: the bias-balanced
- * router the Transformers docs ("Dots3Note", model outputs, aux_loss entry)
+ * router the Transformers documentation ("Dots 3 Note Preview", model outputs, aux_loss entry)
  * name for DeepSeek-V3 and derived models.
  *   s[e] = f32(1 / (1 + exp(-l[e])))  (evaluated in double, rounded once)
  *   b[e] = f32(s[e] + score_bias[e])  (score_bias may be NULL: no bias)
@@ -144,6 +152,8 @@ dmoe_status dmoe_route_grouped(const float* logits, int32_t T, int32_t E, int32_
  * are the unbiased s of the selected experts, divided by their sum when
  * renormalize != 0, times routed_scaling_factor, rounded to FP32.
  * score_bias: [E] FP32 device array. Same requirements as dmoe_route_grouped.
+ * Source: Transformers documentation "Dots 3 Note Preview", model outputs, aux_loss
+ * entry (routers that balance their experts with a bias).
  */
 dmoe_status dmoe_route_sigmoid(const float* logits, const float* score_bias, int32_t T, int32_t E, int32_t K,
                                int32_t n_group, int32_t topk_group, int32_t renormalize, float routed_scaling_factor,
@@ -158,6 +168,10 @@ dmoe_status dmoe_route_sigmoid(const float* logits, const float* score_bias, int
  * token_row [T*K] (row of pair (t, k), or -1 if its expert is not local).
  * Expert ids outside [e0, e0 + E_loc) are simply not local.
  * ws: device workspace of at least dmoe_permute_ws_bytes(T, K, E_loc) bytes.
+ * Source: the pages do not describe how the MoE runner lays out its rows
+ * (SGLang cookbook "Dots3-Note", Configuration Tips, MoE runner paragraph,
+ * names grouped expert GEMMs only). Reading: a stable counting sort by local
+ * expert, which makes every table unique and is all a grouped GEMM needs.
  */
 size_t dmoe_permute_ws_bytes(int32_t T, int32_t K, int32_t E_loc);
 dmoe_status dmoe_permute(const int32_t* topk_ids, int32_t T, int32_t K, int32_t e0, int32_t E_loc,
@@ -174,6 +188,10 @@ dmoe_status dmoe_permute(const int32_t* topk_ids, int32_t T, int32_t K, int32_t 
  * x: [rows, ldx] BF16; q: [rows, ldq] uint8 codes (columns [cols, round_up(cols,
  * 128)) are written as 0x00 and must fit in ldq); scales: [rows, lds] FP32
  * with ceil(cols/128) valid entries per row. Requires cols % 8 == 0.
+ * Source: Transformers PR #47844 "Add dots3-note Preview model support", implementation list
+ * (fine-grained FP8: E4M3 with dynamically quantised activations) and
+ * Validation list (partial blocks). The 1x128 slice, amax/448 and
+ * round-to-nearest-even are this library's reading of "dynamic activations".
  */
 dmoe_status dmoe_quant_act(const uint16_t* x, int32_t rows, int32_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
                            float* scales, int64_t lds, hipStream_t stream);
@@ -185,6 +203,9 @@ dmoe_status dmoe_quant_act(const uint16_t* x, int32_t rows, int32_t cols, int64_
  * q: [round_up(rows, 128), ldq] codes, ldq >= round_up(cols, 128); padding rows
  * and columns are written as 0x00. scales: [ceil(rows/128), ceil(cols/128)]
  * FP32 dense. Requires cols % 4 == 0, ldw % 4 == 0.
+ * Source: Transformers PR #47844 "Add dots3-note Preview model support", implementation list
+ * (E4M3 weights with one scale per 128x128 block) and the authors' reply on
+ * partial weight blocks.
  */
 dmoe_status dmoe_quant_weight_blocks(const float* w, int32_t rows, int32_t cols, int64_t ldw, uint8_t* q,
                                      int64_t ldq, float* scales, hipStream_t stream);
@@ -207,6 +228,11 @@ dmoe_status dmoe_quant_weight_blocks(const float* w, int32_t rows, int32_t cols,
  * 4 GiB (without row_token the check is max_rows * lda * element size, done
  * here); DMOE_ERR_UNSUPPORTED when an expert's weights span more than 4 GiB.
  * ws: at least dmoe_gemm_ws_bytes(max_rows, E_loc).
+ * Source: Transformers documentation "Dots 3 Note Preview", Dots3NoteTextConfig
+ * hidden_act (silu), mlp_bias (no bias on gate_proj, up_proj, down_proj),
+ * moe_intermediate_size; model card "dots-studio/dots3-note-prev", Model
+ * Overview table (256 experts of width 1536 on hidden 5120); Transformers PR #47844 "Add dots3-note Preview model support",
+ * implementation list (fine-grained FP8 GEMMs with 128x128 weight blocks).
  */
 size_t dmoe_gemm_ws_bytes(int32_t max_rows, int32_t E_loc);
 dmoe_status dmoe_grouped_gemm_gateup(int32_t dtype, const void* a, int64_t lda, const float* a_scales,
@@ -222,6 +248,9 @@ dmoe_status dmoe_grouped_gemm_gateup(int32_t dtype, const void* a, int64_t lda, 
  * slice may be partial; padded columns of h and Wd are zero).
  * h: [max_rows, ldh] BF16 or E4M3 codes (+ h_scales [max_rows, ldhs]);
  * o: [max_rows, ldo] BF16.
+ * Source: as dmoe_grouped_gemm_gateup (down_proj of the same expert). On the
+ * FP8 path h is quantised like any activation before this call (Transformers PR #47844 "Add dots3-note Preview model support",
+ * implementation list: dynamically quantised activations).
  */
 dmoe_status dmoe_grouped_gemm_down(int32_t dtype, const void* h, int64_t ldh, const float* h_scales, int64_t ldhs,
                                    const int32_t* offsets, int32_t E_loc, int32_t max_rows, const void* w_down,
@@ -235,6 +264,10 @@ dmoe_status dmoe_grouped_gemm_down(int32_t dtype, const void* h, int64_t ldh, co
  * with one group of T_s rows and the identity row map. a/a_scales as in the
  * gate/up call; weights in the single-expert layout above; s_out [T_s, lds_out].
  * ws: at least dmoe_shared_expert_ws_bytes(dtype, T_s, H, F_s).
+ * Source: Transformers documentation "Dots 3 Note Preview", Dots3NoteTextConfig
+ * n_shared_experts (1) and shared_experts_intermediate_size; model card
+ * "dots-studio/dots3-note-prev", Model Overview table (1 shared expert). Its
+ * output enters the sum with weight 1 (the config gives it no gate).
  */
 size_t dmoe_shared_expert_ws_bytes(int32_t dtype, int32_t T_s, int32_t H, int32_t F_s);
 dmoe_status dmoe_shared_expert(int32_t dtype, const void* a, int64_t lda, const float* a_scales, int64_t ldas,
@@ -250,6 +283,10 @@ dmoe_status dmoe_shared_expert(int32_t dtype, const void* a, int64_t lda, const 
  * accumulated in FP32 in slot order, no atomics. s_out may be NULL (T_s
  * ignored). o: [*, ldo] BF16; y: [T, ldy] BF16. Requires 1 <= K <= 64 and
  * H % 8 == 0.
+ * Source: Transformers documentation "Dots 3 Note Preview", Dots3NoteTextConfig
+ * norm_topk_prob and routed_scaling_factor (the weights applied here) and
+ * n_shared_experts (the shared output, added with weight 1). The pages fix no
+ * summation order; FP32 in slot order is this library's reading.
  */
 dmoe_status dmoe_combine(const uint16_t* o, int64_t ldo, const int32_t* token_row, const float* topk_w,
                          const uint16_t* s_out, int64_t lds, int32_t T_s, int32_t T, int32_t K, int32_t H,
@@ -306,6 +343,19 @@ typedef struct dmoe_layer_ptrs {
   int64_t ldy;
 } dmoe_layer_ptrs;
 
+/*
+ * Whole layer on one stream: the steps above in order, reading desc and ptrs
+ * (host structs, not retained). ws: device workspace of at least
+ * dmoe_forward_ws_bytes(desc) bytes, 16-byte aligned; its contents after the
+ * call can be inspected with dmoe_forward_ws_offset. dmoe_forward_ws_bytes
+ * returns 0 for an invalid desc.
+ * Source: the MoE block as Transformers documentation "Dots 3 Note Preview"
+ * configures it (Dots3NoteTextConfig n_routed_experts 256, n_shared_experts
+ * 1, num_experts_per_tok 8, hidden_size 5120, moe_intermediate_size 1536) and
+ * the model card "dots-studio/dots3-note-prev", Model Overview table; FP8 as
+ * in Transformers PR #47844 "Add dots3-note Preview model support", implementation list. The pages
+ * describe no workspace: its layout is this library's own.
+ */
 size_t dmoe_forward_ws_bytes(const dmoe_layer_desc* desc);
 dmoe_status dmoe_forward(const dmoe_layer_desc* desc, const dmoe_layer_ptrs* ptrs, void* ws, size_t ws_bytes,
                          hipStream_t stream);
@@ -323,6 +373,7 @@ dmoe_status dmoe_forward(const dmoe_layer_desc* desc, const dmoe_layer_ptrs* ptr
  * event is a stream marker that costs a few microseconds of queue time).
  * Recording events adds stream markers only; the results are identical to
  * dmoe_forward.
+ * Source: as dmoe_forward.
  */
 #define DMOE_STAGES 9
 dmoe_status dmoe_forward_timed(const dmoe_layer_desc* desc, const dmoe_layer_ptrs* ptrs, void* ws, size_t ws_bytes,

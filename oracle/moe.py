@@ -7,7 +7,7 @@ What the layer computes, and where the pages fix it:
 
 * Shape: 256 routed experts plus 1 shared expert, top-8, hidden 5120, expert
   FFN 1536 (model card "dots-studio/dots3-note-prev", Model Overview table;
-  Transformers docs "Dots3Note", Dots3NoteTextConfig: ``n_routed_experts``,
+  Transformers documentation "Dots 3 Note Preview", Dots3NoteTextConfig: ``n_routed_experts``,
   ``n_shared_experts``, ``num_experts_per_tok``, ``moe_intermediate_size``,
   ``shared_experts_intermediate_size``).
 * Router: token-choice top-k, ``norm_topk_prob`` true (renormalise the kept
@@ -211,7 +211,7 @@ def dequantize_weight_blocks(q: np.ndarray, s: np.ndarray) -> np.ndarray:
 def router_logits(x: np.ndarray, w_r: np.ndarray) -> np.ndarray:
     """FP32 router logits L[t, e] = sum_h x[t, h] * W_r[e, h], summed in float64, stored as float32.
 
-    Router output shape (batch*seq, num_experts): Transformers docs "Dots3Note",
+    Router output shape (batch*seq, num_experts): Transformers documentation "Dots 3 Note Preview",
     ``router_logits`` output entry; FP32 routing: PR #47844 implementation list.
     parity pinned (brute force, special weights).
     """
@@ -224,7 +224,7 @@ def route(logits: np.ndarray, k: int, n_group: int = 1, topk_group: int | None =
 
     Selection: the k largest FP32 logits; equal values go to the lower expert
     index; -0.0 is treated as +0.0; slot j holds the expert of rank j.
-    Group-limited selection (Transformers docs "Dots3Note", Dots3NoteTextConfig
+    Group-limited selection (Transformers documentation "Dots 3 Note Preview", Dots3NoteTextConfig
     ``n_group``, ``topk_group``; 1 and 1 by default, i.e. ungrouped): the E
     experts form n_group groups of E/n_group consecutive experts, a group's
     score is its largest logit (the docs fix only that the chosen experts lie
@@ -267,7 +267,7 @@ def sigmoid_scores(logits: np.ndarray) -> np.ndarray:
 def route_sigmoid(logits: np.ndarray, k: int, bias: np.ndarray | None = None, n_group: int = 1,
                   topk_group: int | None = None, renormalize: bool = True,
                   scaling: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
-    """Sigmoid scoring with a selection-only correction bias, as in the routers the Transformers docs ("Dots3Note",
+    """Sigmoid scoring with a selection-only correction bias, as in the routers the Transformers documentation ("Dots 3 Note Preview",
     model outputs, ``aux_loss`` entry) describe as balancing their experts with a router bias (DeepSeek-V3 and
     its derivatives); written from that published rule.
 
@@ -348,10 +348,12 @@ def swiglu_expert(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
     return bf16_round(h @ wd.T)
 
 
-def combine(o: np.ndarray, token_row: np.ndarray, w: np.ndarray, s: np.ndarray | None, t_s: int) -> np.ndarray:
+def combine(o: np.ndarray, token_row: np.ndarray, w: np.ndarray, s: np.ndarray | None, t_s: int,
+            rounded: bool = True) -> np.ndarray:
     """y[t] = bf16( sum_k w[t,k] * o[token_row[t,k]] + (t < T_s ? s[t] : 0) ), summed in float64.
 
-    Pairs with token_row < 0 (expert on another GPU) contribute nothing.
+    Pairs with token_row < 0 (expert on another GPU) contribute nothing. With
+    ``rounded=False`` the float64 sum is returned before its one BF16 rounding.
     """
     T, K = token_row.shape
     H = o.shape[1] if o.size else (s.shape[1] if s is not None else 0)
@@ -362,7 +364,7 @@ def combine(o: np.ndarray, token_row: np.ndarray, w: np.ndarray, s: np.ndarray |
         acc[m] += np.asarray(w, dtype=np.float64)[m, k][:, None] * o[r[m]]
     if s is not None and t_s > 0:
         acc[:t_s] += s[:t_s]
-    return bf16_round(acc)
+    return bf16_round(acc) if rounded else acc
 
 
 # ---------------------------------------------------------------------------
@@ -378,6 +380,7 @@ class OracleResult:
     x_codes: np.ndarray | None  # [n, H] uint8 (FP8 path)
     x_scales: np.ndarray | None
     y: np.ndarray               # [n, H] float64 (bfloat16 values)
+    y_sum: np.ndarray           # [n, H] float64: the combine's sum before its BF16 rounding
 
 
 def _expert_weights(cfg, weights: Callable, e: int, fp8: bool):
@@ -438,8 +441,8 @@ def moe_forward(cfg, x_bits: np.ndarray, weights: Callable, w_r: np.ndarray | No
     if shared_rows.any():
         wg, wu, wd = _expert_weights(cfg, weights, -1, fp8)
         s[shared_rows] = swiglu_expert(a_all[shared_rows], wg, wu, wd, fp8)
-    y = combine(o, token_row, w, s, tok.size)  # rows of s past T_s are zero
-    return OracleResult(tok, L, ids, w, xq, xs, y)
+    y_sum = combine(o, token_row, w, s, tok.size, rounded=False)  # rows of s past T_s are zero
+    return OracleResult(tok, L, ids, w, xq, xs, bf16_round(y_sum), y_sum)
 
 
 def moe_forward_loops(cfg, x_bits, weights: Callable, w_r=None, logits=None) -> np.ndarray:

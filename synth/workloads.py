@@ -2,8 +2,8 @@
 
 Shapes follow the dots3-note preview MoE layer: hidden 5120, 256 routed experts
 plus 1 shared expert, top-8, per-expert FFN 1536 (model card
-"dots-studio/dots3-note-prev", Model Overview table; Transformers docs
-"Dots3Note", Dots3NoteTextConfig parameters ``hidden_size``,
+"dots-studio/dots3-note-prev", Model Overview table; Transformers documentation
+"Dots 3 Note Preview", Dots3NoteTextConfig parameters ``hidden_size``,
 ``n_routed_experts``, ``n_shared_experts``, ``num_experts_per_tok``,
 ``moe_intermediate_size``, ``shared_experts_intermediate_size``).
 
@@ -92,7 +92,7 @@ CONFIGS = [
                 dtype="fp8", T_s=2048, logits="zipf"),
     LayerConfig("nondiv_fp8", T=2048, H=5120, F=1400, F_s=1400, E=256, E_loc=256, e0=0, K=8,
                 dtype="fp8", T_s=2048, logits="uniform"),
-    # Vision-tower MoE (Transformers docs "Dots3Note", Dots3NoteVisionConfig: hidden_size 1536,
+    # Vision-tower MoE (Transformers documentation "Dots 3 Note Preview", Dots3NoteVisionConfig: hidden_size 1536,
     # moe_intermediate_size 2112, num_local_experts 64, FP32 router; no shared expert). The docs leave
     # num_experts_per_tok unset; the text model's top-8 is used. 2112 = 16.5 x 128: a partial FP8 block.
     LayerConfig("vision_bf16", T=4096, H=1536, F=2112, F_s=0, E=64, E_loc=64, e0=0, K=8,

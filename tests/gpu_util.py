@@ -86,31 +86,33 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
     return np.where(a > 0, np.ldexp(1.0, np.maximum(e - 8, -133)), 0.0)
 
 
-def compare_y(y_gpu: np.ndarray, y_ref: np.ndarray, what: str = "y") -> tuple[float, float]:
-    """Layer-output tolerance: relative L2 <= 5e-3 and max abs error <= 2e-2 * RMS(y_ref).
+def compare_y(y_gpu: np.ndarray, y_ref: np.ndarray, y_sum: np.ndarray, what: str = "y") -> tuple[float, float]:
+    """Layer-output tolerance: relative L2 <= 5e-3 against the oracle's BF16 y, and for EVERY element
+    |y_gpu - y_sum| <= 2e-2 * RMS(y_ref) + ulp_bf16 / 2, where y_sum is the oracle's float64 combine sum
+    before its one BF16 rounding.
 
-    y is BF16 on both sides, each the rounding of a nearby real value, so two
-    correct results of one element can differ by one BF16 ulp of that element
-    whatever their pre-rounding distance; at |y| >= 2.56 RMS a single ulp
-    already exceeds 2e-2 RMS. The max-abs bound is therefore applied per
-    element on top of that granularity: |dy| <= 2e-2 * RMS + ulp_bf16(y_ref).
-    The literal max |dy| / RMS is reported alongside.
+    The half ulp is the GPU's own final rounding: the GPU output is the BF16 rounding of a value near y_sum,
+    and that rounding moves it by at most half a BF16 ulp (taken at the larger of |y_gpu| and |y_sum|, which
+    covers a rounding up into the next binade). Everything else, i.e. the distance of the GPU's unrounded
+    value from the oracle's, must stay within 2e-2 RMS. The literal max |y_gpu - y_ref| / RMS is reported.
     """
     y_gpu = np.asarray(y_gpu, np.float64)
     y_ref = np.asarray(y_ref, np.float64)
+    y_sum = np.asarray(y_sum, np.float64)
+    assert y_gpu.shape == y_ref.shape == y_sum.shape, f"{what}: shapes differ"
     assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite GPU output"
+    if y_ref.size == 0:
+        return 0.0, 0.0
     rms = float(np.sqrt(np.mean(y_ref ** 2)))
-    err = np.abs(y_gpu - y_ref)
     rel = float(np.linalg.norm(y_gpu - y_ref) / max(np.linalg.norm(y_ref), 1e-300))
-    mx = float(err.max() / max(rms, 1e-300)) if y_ref.size else 0.0
-    bound = MAX_ABS_OVER_RMS * rms + bf16_ulp(y_ref)
-    over = float(np.mean(err > MAX_ABS_OVER_RMS * rms)) if y_ref.size else 0.0
-    worst = float(np.max(err / np.maximum(bound, 1e-300))) if y_ref.size else 0.0
-    say(f"  {what}: rel_l2={rel:.3e} max_abs/rms={mx:.3e} (elements over 2e-2 RMS: {over:.2e}; "
-        f"max |dy|/(2e-2 RMS + ulp) = {worst:.3f}; n={y_ref.size})")
+    mx = float(np.abs(y_gpu - y_ref).max() / max(rms, 1e-300))
+    err = np.abs(y_gpu - y_sum)
+    bound = MAX_ABS_OVER_RMS * rms + 0.5 * bf16_ulp(np.maximum(np.abs(y_gpu), np.abs(y_sum)))
+    worst = float(np.max(err / np.maximum(bound, 1e-300)))
+    say(f"  {what}: rel_l2={rel:.3e} max|y-y_ref|/rms={mx:.3e} "
+        f"max |y-y_sum|/(2e-2 RMS + ulp/2) = {worst:.3f} (n={y_ref.size})")
     assert rel <= REL_L2, f"{what}: relative L2 error {rel:.3e} > {REL_L2}"
-    assert worst <= 1.0, f"{what}: an element differs by more than 2e-2 RMS + 1 BF16 ulp ({worst:.3f} x bound)"
-    assert over <= 1e-2, f"{what}: {over:.2e} of the elements exceed 2e-2 RMS"
+    assert worst <= 1.0, f"{what}: an element is further than 2e-2 RMS + ulp/2 from the oracle ({worst:.3f} x)"
     return rel, mx
 
 

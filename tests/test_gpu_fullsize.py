@@ -85,7 +85,7 @@ def test_full_size_workload(ci):
         xs = layer.ws_view(d, ws, "x_scales").cpu().numpy()[tok]
         np.testing.assert_array_equal(xq, ref.x_codes)
         np.testing.assert_array_equal(xs, ref.x_scales)
-    compare_y(y[tok][keep], ref.y[keep], f"y sampled ({keep.size} tokens)")
+    compare_y(y[tok][keep], ref.y[keep], ref.y_sum[keep], f"y sampled ({keep.size} tokens)")
     del layer, out, ws
     gc.collect()
     torch.cuda.empty_cache()

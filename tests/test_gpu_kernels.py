@@ -274,9 +274,13 @@ def test_combine(T, K, H, T_s, local_frac):
     y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
     s_dev = to_dev_bf16(s_bits) if T_s else None
     dm.dmoe_combine(to_dev_bf16(o_bits), torch.from_numpy(tr).to(DEV), torch.from_numpy(w).to(DEV), s_dev, T_s, H, y)
-    ref = oracle.combine(oracle.bf16_to_f64(o_bits), tr, w, oracle.bf16_to_f64(s_bits) if T_s else None, T_s)
+    o64, s64 = oracle.bf16_to_f64(o_bits), (oracle.bf16_to_f64(s_bits) if T_s else None)
+    ref = oracle.combine(o64, tr, w, s64, T_s)
+    y_sum = oracle.combine(o64, tr, w, s64, T_s, rounded=False)
+    mag = oracle.combine(np.abs(o64), tr, np.abs(w), None if s64 is None else np.abs(s64), T_s, rounded=False)
     got = bf16_values(y)
-    # FP32 accumulation vs FP64: equal up to one BF16 rounding flip on rare elements
-    ulp = np.abs(ref) * 2.0 ** -7 + 1e-30
-    assert np.all(np.abs(got - ref) <= ulp)
+    # FP32 accumulation of at most K + 1 terms, then one BF16 rounding of the FP32 sum
+    a = np.maximum(np.abs(got), np.abs(y_sum))
+    half_ulp = np.where(a > 0, np.ldexp(1.0, np.maximum(np.frexp(a)[1] - 9, -134)), 0.0)
+    assert np.all(np.abs(got - y_sum) <= half_ulp + (K + 2) * 2.0 ** -24 * mag)
     assert np.mean(got == ref) > 0.99

@@ -118,7 +118,7 @@ def _check_given_logits_path(cfg, layer, x, ref, logits_np):
     # rows with no local pair and no shared expert are exactly zero on both sides
     idle = ~np.any(tr_r >= 0, axis=1) & (np.arange(cfg.T) >= cfg.T_s)
     assert np.all(y[idle] == 0) and np.all(ref.y[idle] == 0)
-    compare_y(y[~idle], ref.y[~idle], "y (given logits)")
+    compare_y(y[~idle], ref.y[~idle], ref.y_sum[~idle], "y (given logits)")
     return out
 
 
@@ -141,7 +141,7 @@ def test_forward_matches_oracle(name):
     diff = near_tie_tokens(ids, ref.ids, ref.logits, 2 * LOGIT_TOL)
     keep = np.setdiff1d(np.arange(cfg.T), diff)
     assert diff.size <= max(1, cfg.T // 100), f"{diff.size} tokens routed differently"
-    compare_y(bf16_values(out["y"])[keep], ref.y[keep], "y (own logits)")
+    compare_y(bf16_values(out["y"])[keep], ref.y[keep], ref.y_sum[keep], "y (own logits)")
 
 
 def test_forward_is_deterministic():

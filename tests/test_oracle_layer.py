@@ -142,3 +142,16 @@ def test_parameter_count_closed_form_from_pages():
     assert g["total_parameters"] > routed > 0.9 * g["total_parameters"]
     assert active < g["activated_parameters"] and active > 0.5 * g["activated_parameters"]
     assert L * E * 2 * H * F < 0.7 * g["total_parameters"]
+
+
+def test_combine_hand_example():
+    """Two tokens, two slots, H = 2: token 0 mixes rows 0 and 2 with weights 1/4 and 3/4 and adds the shared
+    row (T_s = 1); token 1's second slot is on another GPU (-1) and it gets no shared row. The float64 sum
+    1.75390625 lies halfway between the bfloat16 values 1.75 and 1.7578125 and rounds to the even 1.75."""
+    o = np.array([[1.0, 3.0], [0.5, -1.0], [2.0, 2.0]])
+    token_row = np.array([[0, 2], [1, -1]], np.int32)
+    w = np.array([[0.25, 0.75], [1.0, 0.5]], np.float32)
+    s = np.array([[1.0 / 256, 0.0], [7.0, 7.0]])
+    y_sum = oracle.combine(o, token_row, w, s, 1, rounded=False)
+    np.testing.assert_array_equal(y_sum, [[1.75390625, 2.25], [0.5, -1.0]])
+    np.testing.assert_array_equal(oracle.combine(o, token_row, w, s, 1), [[1.75, 2.25], [0.5, -1.0]])
