@@ -67,6 +67,14 @@ dmoe_status check_pitch(int64_t ld, int64_t min_ld, int elem, const char* name) 
 
 }  // namespace
 
+dmoe_status dmoe::set_error(dmoe_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
 extern "C" {
 
 const char* dmoe_last_error(void) { return g_err; }
@@ -632,6 +640,13 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
     g1.xws0 = p->sws_gate;
     g1.xws1 = p->sws_up;
   }
+  // FP8 with the wide tile kernel: h is quantised in the gate/up epilogue
+  const bool fused_quant = fp8 && gemm_fuses_h_quant(mcap, d->E_loc);
+  if (fused_quant) {
+    g1.out_q = at(W_HQ);
+    g1.out_s = reinterpret_cast<float*>(at(W_HS));
+    g1.ld_s = ceil_div(d->F, 128);
+  }
   STEP(launch_gemm_gateup(g1, stream), "gateup");
   STEP(mark(), "event");
 
@@ -642,7 +657,10 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
     uint8_t* hq = at(W_HQ);
     float* hs = reinterpret_cast<float*>(at(W_HS));
     ldhs = ceil_div(d->F, 128);
-    STEP(launch_quant_act(h, mcap + xrows, d->F, fpad, hq, fpad, hs, ldhs, stream), "quant h");
+    // rows [M, T*K) were never written by gate/up: skipped (M read on the device)
+    if (!fused_quant)
+      STEP(launch_quant_act(h, mcap + xrows, d->F, fpad, hq, fpad, hs, ldhs, stream, offsets + d->E_loc, mcap),
+           "quant h");
     ha = hq;
     hsc = hs;
   }

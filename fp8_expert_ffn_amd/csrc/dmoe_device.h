@@ -102,6 +102,12 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  const uint32_t lo = __shfl((uint32_t)v, src);
+  const uint32_t hi = __shfl((uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ double shfl_xor_f64(double v, int off) {
   const uint64_t b = (uint64_t)__double_as_longlong(v);
   return __longlong_as_double((long long)shfl_xor_u64(b, off));

@@ -11,6 +11,9 @@
 
 namespace dmoe {
 
+// Sets the calling thread's dmoe_last_error text and returns `code` (api.hip).
+dmoe_status set_error(dmoe_status code, const char* fmt, ...);
+
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }
 
@@ -52,8 +55,10 @@ hipError_t launch_permute(const int32_t* ids, int T, int K, int e0, int E_loc, i
                           hipStream_t stream);
 
 // quant.hip
+// skip_from (device pointer, may be null): rows [*skip_from, skip_to) are not touched
 hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int64_t ldx, uint8_t* q, int64_t ldq,
-                            float* scales, int64_t lds, hipStream_t stream);
+                            float* scales, int64_t lds, hipStream_t stream, const int32_t* skip_from = nullptr,
+                            int skip_to = 0);
 hipError_t launch_quant_weight_blocks(const float* w, int rows, int cols, int64_t ldw, uint8_t* q, int64_t ldq,
                                       float* scales, hipStream_t stream);
 
@@ -89,12 +94,20 @@ struct GemmArgs {
   const void* xw1 = nullptr;
   const float* xws0 = nullptr;
   const float* xws1 = nullptr;
+  // FP8 gate/up only, when gemm_fuses_h_quant(): quantise h in the epilogue
+  // into codes out_q [rows, ldo] and scales out_s [rows, ld_s] instead of
+  // writing BF16 h to out
+  uint8_t* out_q = nullptr;
+  float* out_s = nullptr;
+  int64_t ld_s = 0;
 };
 size_t gemm_ws_bytes(int max_rows, int E_loc, int extra_rows = 0);
 hipError_t launch_schedule(const int32_t* offsets, int E_loc, int max_rows, int extra_rows, int extra_row0,
                            void* ws, hipStream_t stream);
 // true when launch_gemm_* picks the weight-streaming kernel (it needs no tile schedule)
 bool gemm_uses_stream(int max_rows, int E_loc);
+// true when the FP8 gate/up launch can quantise h in its epilogue (GemmArgs.out_q)
+bool gemm_fuses_h_quant(int max_rows, int E_loc);
 hipError_t launch_gemm_gateup(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_fill_offsets(int32_t* offsets, int rows, hipStream_t stream);

@@ -61,15 +61,6 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
   if (t == (int)blockDim.x - 1) *ntiles = min(routed + nx, cap);
 }
 
-// Operand modes of the tile kernel. Every mode moves 128-byte K rows through LDS.
-//  kModeBF16: BF16 operands, 64 K per stage, BF16 MFMA.
-//  kModeFP8X: E4M3 operands, 128 K per stage (one scale slice); fragments are
-//             converted exactly to BF16 after the LDS read and multiplied on
-//             BF16 matrix cores: every product is exact and the slice's sum is
-//             accumulated in FP32 before the a_scale * w_scale promotion.
-//  kModeFP8:  E4M3 operands, 128 K per stage (one scale slice), FP8 MFMA
-//             (the matrix core's own accumulation precision within a slice).
-constexpr int kModeBF16 = 0, kModeFP8X = 1, kModeFP8 = 2;
 
 // Tile kernel. A workgroup (2 x WN waves) owns kBM = 128 rows of one group and
 // 16 * NT * WN weight rows (gate/up: 8 * NT * WN gate + as many up rows, i.e.
@@ -86,15 +77,6 @@ constexpr int kModeBF16 = 0, kModeFP8X = 1, kModeFP8 = 2;
 // bytes with 16-byte units XOR-swizzled (swz in gemm_common.h) so that the
 // fragment reads are free of bank conflicts. Grid: 1-D, tile-major, column
 // block fastest.
-
-// Wave-uniform copy of a pointer (lets the compiler use scalar loads through it).
-template <typename T>
-__device__ __forceinline__ const T* uniform_ptr(const T* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
-}
 
 // Build-time tuning knobs; the defaults are the measured best on gfx950 (the
 // alternatives stay buildable for re-measurement): ring depth NS (2 with two
@@ -501,8 +483,15 @@ hipError_t launch_fill_offsets(int32_t* offsets, int rows, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Rows per tile of the schedule: the wide kernel's 256 (default) or this file's 128.
+#ifndef DMOE_TILE_WIDE
+#define DMOE_TILE_WIDE 1
+#endif
+static int tile_bm() { return DMOE_TILE_WIDE ? kWideBM : kBM; }
+
 static int tile_cap(int max_rows, int E_loc, int extra_rows) {
-  return (int)(ceil_div(max_rows, kBM) + E_loc + ceil_div(extra_rows, kBM));
+  const int bm = tile_bm();
+  return (int)(ceil_div(max_rows, bm) + E_loc + ceil_div(extra_rows, bm));
 }
 
 size_t gemm_ws_bytes(int max_rows, int E_loc, int extra_rows) {
@@ -517,12 +506,14 @@ static int32_t* sched_count(void* ws, int cap) {
 hipError_t launch_schedule(const int32_t* offsets, int E_loc, int max_rows, int extra_rows, int extra_row0,
                            void* ws, hipStream_t stream) {
   const int cap = tile_cap(max_rows, E_loc, extra_rows);
-  schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E_loc, kBM, extra_rows, extra_row0, cap, sched_tiles(ws),
+  schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E_loc, tile_bm(), extra_rows, extra_row0, cap, sched_tiles(ws),
                                           sched_count(ws, cap));
   return hipGetLastError();
 }
 
 bool gemm_uses_stream(int max_rows, int E_loc) { return ceil_div(max_rows, E_loc) <= 32; }
+
+bool gemm_fuses_h_quant(int max_rows, int E_loc) { return DMOE_TILE_WIDE && !gemm_uses_stream(max_rows, E_loc); }
 
 static hipError_t launch_gemm(const GemmArgs& g, bool gateup, hipStream_t stream) {
   const int cap = tile_cap(g.max_rows, g.E_loc, g.x_rows);
@@ -564,11 +555,15 @@ static hipError_t launch_gemm(const GemmArgs& g, bool gateup, hipStream_t stream
   p.xws0 = g.xws0;
   p.xws1 = g.xws1;
   p.x_chunk = 0;
+  p.out_q = g.out_q;
+  p.out_s = g.out_s;
+  p.ld_s = g.ld_s;
   // Few rows per expert on average: stream the weights (the tile schedule is not used).
   if (use_stream) {
     p.x_chunk = per_expert <= 16 ? 16 : 32;
     return launch_gemm_stream(p, g.dtype, gateup, (int)per_expert, (int)npad, g.E_loc, stream);
   }
+  if (DMOE_TILE_WIDE) return launch_gemm_wide(p, g.dtype, gateup, (int)npad, cap, stream);
   // tile kernel: 128-byte stages for every mode (FP8: one 128-wide slice, BF16: 64 elements)
   constexpr int NT_GU = DMOE_TILE_NT_GATEUP, NT_DN = DMOE_TILE_NT_DOWN;
   constexpr int WN_GU = DMOE_TILE_WN_GATEUP, WN_DN = DMOE_TILE_WN_DOWN;

@@ -10,6 +10,7 @@ namespace dmoe {
 
 constexpr int kBM = 128;            // rows per tile
 constexpr int kKB = 128;            // K bytes per stage
+constexpr int kWideBM = 256;        // rows per tile of the wide kernel (gemm_wide.hip)
 constexpr int kMaxSlices = 128;     // FP8 tile kernel: at most 128 scale slices along K (K <= 16384)
 
 struct TileArgs {
@@ -38,6 +39,11 @@ struct TileArgs {
   const uint8_t* xw1;
   const float* xws0;
   const float* xws1;
+  // FP8 gate/up in the layer: h quantised in the epilogue (1x128 rule) into
+  // codes out_q [rows, ldo] and scales out_s [rows, ld_s]; nullptr: BF16 h in out
+  uint8_t* out_q;
+  float* out_s;
+  int64_t ld_s;
 };
 
 // Weights, scales and rows of group g: a routed expert (g < E_loc) or the extra group.
@@ -77,6 +83,25 @@ __device__ __forceinline__ GroupView group_view(const TileArgs& p, int g) {
 
 __device__ __forceinline__ int64_t a_row(const TileArgs& p, const GroupView& v, int r) {
   return v.gather ? (int64_t)p.row_token[r] : (int64_t)(r - v.a_base);
+}
+
+// Operand modes of the tile kernels. Every mode moves 128-byte K rows through LDS.
+//  kModeBF16: BF16 operands, 64 K per stage, BF16 MFMA.
+//  kModeFP8X: E4M3 operands, 128 K per stage (one scale slice); fragments are
+//             converted exactly to BF16 after the LDS read and multiplied on
+//             BF16 matrix cores: every product is exact and the slice's sum is
+//             accumulated in FP32 before the a_scale * w_scale promotion.
+//  kModeFP8:  E4M3 operands, 128 K per stage (one scale slice), FP8 MFMA
+//             (the matrix core's own accumulation precision within a slice).
+constexpr int kModeBF16 = 0, kModeFP8X = 1, kModeFP8 = 2;
+
+// Wave-uniform copy of a pointer (lets the compiler use scalar loads through it).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
@@ -167,6 +192,7 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+hipError_t launch_gemm_wide(const TileArgs& p, int dtype, bool gateup, int npad, int cap, hipStream_t stream);
 hipError_t launch_gemm_stream(const TileArgs& p, int dtype, bool gateup, int rows_per_expert, int n_pad,
                               int E_loc, hipStream_t stream);
 

@@ -9,62 +9,23 @@
 // +-448, sign bit kept; s == 0 gives all-zero codes. Partial slices and
 // blocks take the amax over their valid elements only.
 #include "dmoe_internal.h"
+#include "quant_common.h"
 
 namespace dmoe {
-
-__device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, b); }
-
-// Division by a slice scale for the E4M3 decision, cheaper than one correctly
-// rounded division per element. Both operands are first scaled by the same
-// power of two so that the divisor lies in [1, 2); with the correctly rounded
-// reciprocal r of the divisor, q = v' r corrected once by the exact residual
-// v' - q s' (a fused multiply-add) is the quotient, and the sign of zero is
-// restored. This is the FMA correction step of Markstein's division
-// (P. Markstein, "Computation of elementary functions on the IBM RISC
-// System/6000 processor", IBM J. Res. Develop. 34(1), 1990): with r the
-// correctly rounded reciprocal, one step q + (v' - q s') r yields the
-// correctly rounded quotient except in rare cases that need a second step. The code chosen from it equals the code of the correctly rounded
-// f32(v / s) for every BF16 v and every scale s = f32(amax / 448) with
-// |v| <= amax (checked exhaustively on gfx950 for all BF16 amax); quotients
-// that differ in the last f32 bit are far below the smallest E4M3 subnormal.
-struct ScaleDiv {
-  float sn, r;
-  int k;
-};
-__device__ __forceinline__ ScaleDiv make_scale_div(float s) {
-  ScaleDiv d;
-  int e;
-  (void)frexpf(s, &e);  // s = m * 2^e, m in [0.5, 1)
-  d.k = 1 - e;
-  d.sn = ldexpf(s, d.k);
-  d.r = __fdiv_rn(1.0f, d.sn);
-  return d;
-}
-__device__ __forceinline__ float scale_div(const ScaleDiv& d, float v) {
-  const float vn = ldexpf(v, d.k);
-  const float q0 = vn * d.r;
-  const float res = fmaf(-q0, d.sn, vn);
-  return copysignf(fmaf(res, d.r, q0), v);
-}
-
-// Four |q| < 464 values to E4M3 codes (byte i = code of q[i]) with the hardware
-// conversion, which rounds to nearest even exactly like e4m3_encode on that
-// range (checked on gfx950 for every binary32 pattern with |q| < 464).
-__device__ __forceinline__ uint32_t e4m3x4_hw(float q0, float q1, float q2, float q3) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
-  return (uint32_t)w;
-}
 
 // 16 lanes per 128-column slice, 8 BF16 values (16 bytes) per lane; a
 // 256-thread workgroup covers G rounds of 16 consecutive slices (slice
 // (blockIdx.x G + u) 16 + lane / 16 in round u). The G loads of a lane are
 // issued before any is used, so a wave has G 16-byte loads per lane in flight
 // (G = 4 on large inputs: prefill quantise-h 0.074 -> 0.062 ms).
+// skip_from != nullptr: rows [*skip_from, skip_to) are left untouched (the
+// layer's routed rows past the real count M, which no GEMM wrote).
 template <int G>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int rows, int cols,
                                                         int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
-                                                        float* __restrict__ scales, int64_t lds) {
+                                                        float* __restrict__ scales, int64_t lds,
+                                                        const int32_t* __restrict__ skip_from, int skip_to) {
+  const int skip_lo = skip_from ? *skip_from : skip_to;
   const int nsl = (cols + 127) >> 7;
   const int64_t total = (int64_t)rows * nsl;
   const int64_t first = (int64_t)blockIdx.x * G * 16 + (threadIdx.x >> 4);
@@ -78,12 +39,14 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
     r[u] = slice / nsl;
     c0[u] = (int)(slice - r[u] * nsl) * 128 + sub * 8;
     // cols % 8 == 0: a chunk is wholly valid or wholly padding
-    if (slice < total && c0[u] < cols) raw[u] = *reinterpret_cast<const i32x4*>(x + r[u] * ldx + c0[u]);
+    const bool skip = r[u] >= skip_lo && r[u] < skip_to;
+    if (slice < total && c0[u] < cols && !skip) raw[u] = *reinterpret_cast<const i32x4*>(x + r[u] * ldx + c0[u]);
     else raw[u] = i32x4{0, 0, 0, 0};
   }
 #pragma unroll
   for (int u = 0; u < G; ++u) {
     if (first + 16 * u >= total) break;  // whole 16-lane groups leave together
+    if (r[u] >= skip_lo && r[u] < skip_to) continue;  // a whole group: one slice is one row
     const bool valid = c0[u] < cols;
     float v[8];
 #pragma unroll
@@ -112,13 +75,15 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 }
 
 hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int64_t ldx, uint8_t* q, int64_t ldq,
-                            float* scales, int64_t lds, hipStream_t stream) {
+                            float* scales, int64_t lds, hipStream_t stream, const int32_t* skip_from, int skip_to) {
   const int64_t slices = (int64_t)rows * ((cols + 127) / 128);
   if (slices == 0) return hipSuccess;
   if (slices >= 65536)
-    quant_act_kernel<4><<<(unsigned)ceil_div(slices, 64), 256, 0, stream>>>(x, rows, cols, ldx, q, ldq, scales, lds);
+    quant_act_kernel<4><<<(unsigned)ceil_div(slices, 64), 256, 0, stream>>>(x, rows, cols, ldx, q, ldq, scales, lds,
+                                                                           skip_from, skip_to);
   else
-    quant_act_kernel<1><<<(unsigned)ceil_div(slices, 16), 256, 0, stream>>>(x, rows, cols, ldx, q, ldq, scales, lds);
+    quant_act_kernel<1><<<(unsigned)ceil_div(slices, 16), 256, 0, stream>>>(x, rows, cols, ldx, q, ldq, scales, lds,
+                                                                           skip_from, skip_to);
   return hipGetLastError();
 }
 

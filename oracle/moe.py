@@ -331,13 +331,16 @@ def _silu(g: np.ndarray) -> np.ndarray:
     return g / (1.0 + np.exp(-g))
 
 
-def swiglu_expert(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, fp8: bool) -> np.ndarray:
+def swiglu_expert(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, fp8: bool,
+                  rounded: bool = True) -> np.ndarray:
     """One expert on rows a: o = bf16(down(q(bf16(silu(a Wg^T) * (a Wu^T))))).
 
     a, wg [F, H], wu [F, H], wd [H, F] are float64 (already dequantised on the
     FP8 path). On the FP8 path the BF16 h is quantised per 1x128 slice and
     dequantised before the down projection. Returns float64 values that are
-    exactly bfloat16. parity pinned (textbook SwiGLU via torch).
+    exactly bfloat16, or with ``rounded=False`` the float64 down projection
+    before its BF16 rounding. parity pinned (textbook SwiGLU via torch; FP8 h
+    step against torch's float8 cast and hand-made values).
     """
     g = a @ wg.T
     u = a @ wu.T
@@ -345,7 +348,8 @@ def swiglu_expert(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
     if fp8:
         qh, sh = quantize_act(h)
         h = dequantize_act(qh, sh)
-    return bf16_round(h @ wd.T)
+    o = h @ wd.T
+    return bf16_round(o) if rounded else o
 
 
 def combine(o: np.ndarray, token_row: np.ndarray, w: np.ndarray, s: np.ndarray | None, t_s: int,

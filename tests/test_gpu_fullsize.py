@@ -18,6 +18,8 @@ from gpu_util import (DEV, LOGIT_TOL, W_TOL, bf16_values, build_layer, compare_y
 
 pytestmark = pytest.mark.gpu
 
+from fp8_expert_ffn_amd import _lib as L  # noqa: E402
+
 SAMPLES = {1: 16, 2: 5, 3: 6, 4: 5, 5: 8, 6: 8, 7: 4, 8: 10, 9: 6}
 
 
@@ -29,6 +31,52 @@ def _sample_tokens(cfg, n):
     while len(picks) < min(n, cfg.T):
         picks.add(int(rng.integers(0, cfg.T)))
     return np.array(sorted(picks))
+
+
+def _expert_o_check(cfg, x_bits, o_rows, tokens, e, what):
+    """GPU expert outputs o (rows for the given tokens) against oracle.swiglu_expert on the same tokens."""
+    x = oracle.bf16_to_f64(np.asarray(x_bits)[tokens])
+    if cfg.dtype == "fp8":
+        a = oracle.dequantize_act(*oracle.quantize_act(x))
+        w = [oracle.dequantize_weight_blocks(*oracle.quantize_weight_blocks(synth.expert_weight_f32(cfg, n, e)))
+             for n in ("gate", "up", "down")]
+    else:
+        a = x
+        w = [oracle.bf16_to_f64(synth.expert_weight_bf16(cfg, n, e)) for n in ("gate", "up", "down")]
+    o_ref = oracle.swiglu_expert(a, *w, fp8=cfg.dtype == "fp8")
+    o_sum = oracle.swiglu_expert(a, *w, fp8=cfg.dtype == "fp8", rounded=False)
+    compare_y(o_rows, o_ref, o_sum, what)
+
+
+def _check_whole_experts(cfg, layer, d, ws, x_bits, offsets):
+    """Expert outputs at full size, where tile positions differ from the reduced tests: the busiest local expert
+    (the first and last row of every 64-row block, i.e. of every wave's rows in every 256-row tile), the smallest
+    touched expert (all rows) and the last partial tile of the shared expert (all rows)."""
+    o = layer.ws_view(d, ws, "o")
+    rt = layer.ws_view(d, ws, "row_token").cpu().numpy()
+    counts = np.diff(offsets)
+    big = int(np.argmax(counts))
+    r0, r1 = int(offsets[big]), int(offsets[big + 1])
+    rel = np.arange(r1 - r0)
+    rows = r0 + rel[(rel % 64 == 0) | (rel % 64 == 63) | (rel == rel[-1])]
+    t0 = time.time()
+    _expert_o_check(cfg, x_bits, bf16_values(o[rows]), rt[rows], cfg.e0 + big,
+                    f"o of the busiest expert {cfg.e0 + big} ({r1 - r0} rows, {rows.size} checked)")
+    touched = np.nonzero(counts)[0]
+    small = int(touched[np.argmin(counts[touched])])
+    s0, s1 = int(offsets[small]), int(offsets[small + 1])
+    _expert_o_check(cfg, x_bits, bf16_values(o[s0:s1]), rt[s0:s1], cfg.e0 + small,
+                    f"o of the smallest expert {cfg.e0 + small} ({s1 - s0} rows)")
+    if cfg.T_s > 0 and cfg.F_s == cfg.F:
+        # shared rows follow the T*K routed rows of o; its last tile of the 256-row schedule
+        mcap = cfg.T * cfg.K
+        first = (cfg.T_s - 1) // 256 * 256
+        start = L.dmoe_forward_ws_offset(d, 9)  # o, routed rows then the shared rows
+        o_all = ws[start:start + (mcap + cfg.T_s) * cfg.H * 2].view(torch.bfloat16).view(-1, cfg.H)
+        _expert_o_check(cfg, x_bits, bf16_values(o_all[mcap + first:mcap + cfg.T_s]),
+                        np.arange(first, cfg.T_s), synth.SHARED,
+                        f"o of the shared expert's last tile (tokens {first}..{cfg.T_s - 1})")
+    say(f"  whole-expert checks in {time.time() - t0:.1f}s")
 
 
 @pytest.mark.parametrize("ci", [1, 2, 3, 4, 5, 6, 7, 8, 9])
@@ -86,6 +134,8 @@ def test_full_size_workload(ci):
         np.testing.assert_array_equal(xq, ref.x_codes)
         np.testing.assert_array_equal(xs, ref.x_scales)
     compare_y(y[tok][keep], ref.y[keep], ref.y_sum[keep], f"y sampled ({keep.size} tokens)")
+    if ci in (2, 3, 4):
+        _check_whole_experts(cfg, layer, d, ws, x_bits, offsets)
     del layer, out, ws
     gc.collect()
     torch.cuda.empty_cache()

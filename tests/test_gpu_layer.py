@@ -84,6 +84,16 @@ CASES = {
                                        dtype="fp8", T_s=40, logits="uniform"),
     "small_ep_bf16": synth.LayerConfig("small_ep", T=16, H=1024, F=256, F_s=256, E=256, E_loc=32, e0=32, K=8,
                                        dtype="bf16", T_s=16, logits="zipf"),
+    # several 256-row tiles per expert on the wide tile GEMM (about 500 rows per expert: a full tile and a
+    # ragged one), and one expert of 257 or 513 rows (a last tile of one row)
+    "wide_tiles_fp8": synth.LayerConfig("wide_tiles_fp8", T=2000, H=512, F=384, F_s=384, E=8, E_loc=8, e0=0, K=2,
+                                        dtype="fp8", T_s=700, logits="router"),
+    "wide_tiles_bf16": synth.LayerConfig("wide_tiles_bf16", T=1500, H=768, F=256, F_s=256, E=6, E_loc=6, e0=0,
+                                         K=2, dtype="bf16", T_s=1500, logits="uniform"),
+    "rows_257_fp8": synth.LayerConfig("rows_257_fp8", T=257, H=512, F=256, F_s=0, E=1, E_loc=1, e0=0, K=1,
+                                      dtype="fp8", T_s=0, logits="single"),
+    "rows_513_bf16": synth.LayerConfig("rows_513_bf16", T=513, H=384, F=128, F_s=128, E=1, E_loc=1, e0=0, K=1,
+                                       dtype="bf16", T_s=513, logits="single"),
 }
 
 
