@@ -33,6 +33,7 @@ EXPORTS = [
     "dmoe_permute", "dmoe_quant_act", "dmoe_quant_weight_blocks", "dmoe_gemm_ws_bytes",
     "dmoe_grouped_gemm_gateup", "dmoe_grouped_gemm_down", "dmoe_shared_expert_ws_bytes", "dmoe_shared_expert",
     "dmoe_combine", "dmoe_forward_ws_bytes", "dmoe_forward", "dmoe_forward_timed", "dmoe_forward_ws_offset",
+    "dmoe_forward_noalloc",
 ]
 DMOE_STAGES = 9
 STAGE_NAMES = ["router_logits", "route", "permute", "quant_x", "gateup", "quant_h", "down", "shared", "combine"]
@@ -91,6 +92,7 @@ _SIGS = {
     "dmoe_forward": ([ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerPtrs), P, SZ, P], I32),
     "dmoe_forward_timed": ([ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerPtrs), P, SZ, P, P], I32),
     "dmoe_forward_ws_offset": ([ctypes.POINTER(LayerDesc), I32], I64),
+    "dmoe_forward_noalloc": ([ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerPtrs), P], I32),
 }
 
 
@@ -280,6 +282,14 @@ def dmoe_forward_ws_offset(desc: LayerDesc, which: int) -> int:
 
 def dmoe_forward(desc: LayerDesc, ptrs: LayerPtrs, ws: torch.Tensor, stream=None) -> None:
     _check(lib().dmoe_forward(ctypes.byref(desc), ctypes.byref(ptrs), ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def dmoe_forward_noalloc(desc: LayerDesc, ptrs: LayerPtrs, stream=None) -> None:
+    """dmoe_forward with the library's own fixed device workspace (no caller buffer, nothing allocated)."""
+    _check(lib().dmoe_forward_noalloc(ctypes.byref(desc), ctypes.byref(ptrs), stream_handle(stream)))
+
+
+DMOE_NOALLOC_WS_BYTES = 24 << 20
 
 
 def dmoe_forward_timed(desc: LayerDesc, ptrs: LayerPtrs, ws: torch.Tensor, events, stream=None) -> None:

@@ -387,6 +387,26 @@ dmoe_status dmoe_forward_timed(const dmoe_layer_desc* desc, const dmoe_layer_ptr
  */
 int64_t dmoe_forward_ws_offset(const dmoe_layer_desc* desc, int32_t which);
 
+/*
+ * dmoe_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The workspace is a fixed device array inside the
+ * library of DMOE_NOALLOC_WS_BYTES (24 MiB): each GPU the library runs on
+ * holds its own copy until the process ends. That covers
+ * dmoe_forward_ws_bytes(desc) of the full-size layer (H 5120, F 1536, 256
+ * experts, top-8) up to 128 tokens in BF16 and FP8 (17.5 MiB); a layer that
+ * needs more returns DMOE_ERR_WORKSPACE and enqueues nothing. The call
+ * allocates and frees nothing. The array's device address is looked up once
+ * per device (the device of `stream`, or the current device for the null
+ * stream) on the first call there. Every call on one GPU shares the array and
+ * it keeps the last call's contents (dmoe_forward_ws_offset offsets index into
+ * it); calls that overlap on one GPU, from several streams or threads, race
+ * on it and must be serialised by the caller. Results equal dmoe_forward's
+ * bit for bit.
+ */
+#define DMOE_NOALLOC_WS_BYTES (24u << 20)
+dmoe_status dmoe_forward_noalloc(const dmoe_layer_desc* desc, const dmoe_layer_ptrs* ptrs, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

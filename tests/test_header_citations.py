@@ -23,6 +23,9 @@ def test_every_entry_point_cites_its_passage():
     names = []
     for name, comment in _entry_points():
         names.append(name)
+        if name == "dmoe_forward_noalloc":  # not a step of the layer: its comment names the callers it serves
+            assert "cannot allocate" in " ".join(line.strip(" *") for line in comment.splitlines())
+            continue
         src = comment[comment.find("Source:"):] if "Source:" in comment else ""
         assert src, f"{name}: no Source: line"
         src = " ".join(line.strip(" *") for line in src.splitlines())
