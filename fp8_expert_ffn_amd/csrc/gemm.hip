@@ -483,40 +483,76 @@ hipError_t launch_fill_offsets(int32_t* offsets, int rows, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Rows per tile of the schedule: the wide kernel's 256 (default) or this file's 128.
-#ifndef DMOE_TILE_WIDE
-#define DMOE_TILE_WIDE 1
+// Which tile kernel a launch uses, and so which of the two schedules in the
+// GEMM workspace: the wide kernel (gemm_wide.hip, 256-row tiles) for BF16
+// operands and the FP8 down projection; this file's kernel (128-row tiles,
+// two workgroups per CU) for the FP8 gate/up projection with exact products,
+// where the two independent workgroups per CU overlap one's E4M3 -> BF16
+// conversions with the other's matrix-core work (measured faster there: prefill
+// gate/up 2.58 vs 2.88 ms). DMOE_WIDE_GU = 1 puts FP8 gate/up on the wide kernel
+// too, with h quantised in its epilogue.
+#ifndef DMOE_WIDE_GU
+#define DMOE_WIDE_GU 0
 #endif
-static int tile_bm() { return DMOE_TILE_WIDE ? kWideBM : kBM; }
-
-static int tile_cap(int max_rows, int E_loc, int extra_rows) {
-  const int bm = tile_bm();
+// The GEMM workspace holds two tile schedules, one per tile height:
+// [tiles of 128 rows][count] [tiles of 256 rows][count].
+static int tile_cap(int bm, int max_rows, int E_loc, int extra_rows) {
   return (int)(ceil_div(max_rows, bm) + E_loc + ceil_div(extra_rows, bm));
+}
+static int64_t sched_bytes(int bm, int max_rows, int E_loc, int extra_rows) {
+  return round_up((int64_t)tile_cap(bm, max_rows, E_loc, extra_rows) * 8, 256) + 256;
+}
+
+// The wide kernel also needs enough rows per expert to fill its 256-row tiles
+// (at least 128 on average; fewer, as in the non-divisible workload's 44-90,
+// leave most of each tile empty) and enough work items to fill the CUs several
+// times over (a dense 4096-row layer's down projection has only 340).
+static bool use_wide(int dtype, bool gateup, int max_rows, int E_loc, int extra_rows, int64_t npad) {
+  if (gateup && dtype == DMOE_FP8_E4M3 && !DMOE_WIDE_GU) return false;
+  const int64_t col_blocks = gateup ? npad / 128 : ceil_div(npad, 256);
+  const int64_t items = (int64_t)tile_cap(kWideBM, max_rows, E_loc, extra_rows) * col_blocks;
+  return ceil_div(max_rows, E_loc) >= 128 && items >= 1024;
 }
 
 size_t gemm_ws_bytes(int max_rows, int E_loc, int extra_rows) {
-  return (size_t)round_up((int64_t)tile_cap(max_rows, E_loc, extra_rows) * 8, 256) + 256;
+  return (size_t)(sched_bytes(kBM, max_rows, E_loc, extra_rows) + sched_bytes(kWideBM, max_rows, E_loc, extra_rows));
 }
 
-static int2* sched_tiles(void* ws) { return static_cast<int2*>(ws); }
-static int32_t* sched_count(void* ws, int cap) {
-  return reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + round_up((int64_t)cap * 8, 256));
+struct Sched {
+  int2* tiles;
+  int32_t* count;
+  int cap;
+};
+static Sched sched_of(void* ws, bool wide, int max_rows, int E_loc, int extra_rows) {
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  if (wide) b += sched_bytes(kBM, max_rows, E_loc, extra_rows);
+  const int bm = wide ? kWideBM : kBM;
+  const int cap = tile_cap(bm, max_rows, E_loc, extra_rows);
+  return Sched{reinterpret_cast<int2*>(b), reinterpret_cast<int32_t*>(b + round_up((int64_t)cap * 8, 256)), cap};
 }
 
 hipError_t launch_schedule(const int32_t* offsets, int E_loc, int max_rows, int extra_rows, int extra_row0,
                            void* ws, hipStream_t stream) {
-  const int cap = tile_cap(max_rows, E_loc, extra_rows);
-  schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E_loc, tile_bm(), extra_rows, extra_row0, cap, sched_tiles(ws),
-                                          sched_count(ws, cap));
-  return hipGetLastError();
+  for (int w = 0; w < 2; ++w) {
+    const Sched s = sched_of(ws, w == 1, max_rows, E_loc, extra_rows);
+    schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E_loc, w ? kWideBM : kBM, extra_rows, extra_row0, s.cap,
+                                            s.tiles, s.count);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 bool gemm_uses_stream(int max_rows, int E_loc) { return ceil_div(max_rows, E_loc) <= 32; }
 
-bool gemm_fuses_h_quant(int max_rows, int E_loc) { return DMOE_TILE_WIDE && !gemm_uses_stream(max_rows, E_loc); }
+bool gemm_fuses_h_quant(int max_rows, int E_loc) {
+  return DMOE_WIDE_GU && !gemm_uses_stream(max_rows, E_loc);
+}
 
 static hipError_t launch_gemm(const GemmArgs& g, bool gateup, hipStream_t stream) {
-  const int cap = tile_cap(g.max_rows, g.E_loc, g.x_rows);
+  const bool wide = use_wide(g.dtype, gateup, g.max_rows, g.E_loc, g.x_rows, round_up(g.N, 128));
+  const Sched sch = sched_of(g.ws, wide, g.max_rows, g.E_loc, g.x_rows);
+  const int cap = sch.cap;
   const int64_t per_expert = ceil_div(g.max_rows, g.E_loc);
   const bool use_stream = gemm_uses_stream(g.max_rows, g.E_loc);
   if (!g.scheduled && !use_stream) {
@@ -533,8 +569,8 @@ static hipError_t launch_gemm(const GemmArgs& g, bool gateup, hipStream_t stream
   p.ldas = g.ldas;
   p.row_token = g.row_token;
   p.offsets = g.offsets;
-  p.tiles = sched_tiles(g.ws);
-  p.ntiles = sched_count(g.ws, cap);
+  p.tiles = sch.tiles;
+  p.ntiles = sch.count;
   p.w0 = static_cast<const uint8_t*>(g.w0);
   p.w1 = static_cast<const uint8_t*>(g.w1);
   p.ldw_b = g.ldw * es;
@@ -563,7 +599,7 @@ static hipError_t launch_gemm(const GemmArgs& g, bool gateup, hipStream_t stream
     p.x_chunk = per_expert <= 16 ? 16 : 32;
     return launch_gemm_stream(p, g.dtype, gateup, (int)per_expert, (int)npad, g.E_loc, stream);
   }
-  if (DMOE_TILE_WIDE) return launch_gemm_wide(p, g.dtype, gateup, (int)npad, cap, stream);
+  if (wide) return launch_gemm_wide(p, g.dtype, gateup, (int)npad, cap, stream);
   // tile kernel: 128-byte stages for every mode (FP8: one 128-wide slice, BF16: 64 elements)
   constexpr int NT_GU = DMOE_TILE_NT_GATEUP, NT_DN = DMOE_TILE_NT_DOWN;
   constexpr int WN_GU = DMOE_TILE_WN_GATEUP, WN_DN = DMOE_TILE_WN_DOWN;

@@ -40,6 +40,15 @@ constexpr int kWWaves = kWThreads / 64;
 #ifndef DMOE_WIDE_GU_FP8
 #define DMOE_WIDE_GU_FP8 0
 #endif
+// look-ahead distance in stages of the L2 touch of future A and weight lines (0: none)
+#ifndef DMOE_WIDE_PF
+#define DMOE_WIDE_PF 0
+#endif
+// scheduling directives that keep the FP8 MFMA / promotion software pipeline in order
+#ifndef DMOE_WIDE_SCHED
+#define DMOE_WIDE_SCHED 0
+#endif
+constexpr int kPF = DMOE_WIDE_PF;
 
 // Relative bound used to decide whether the FP8 matrix cores' h can settle a
 // slice's BF16 amax: the largest relative difference between the slice amax
@@ -219,7 +228,8 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
   __shared__ __attribute__((aligned(256))) float lsa0[kWBM];
   __shared__ __attribute__((aligned(256))) float lsa1[kWBM];
   __shared__ float lsw[2][kMaxSlices];
-  asm volatile("" ::"v"(lds), "v"(lsa0), "v"(lsa1) : "memory");
+  __shared__ __attribute__((aligned(256))) float lscrap[64];  // target of the look-ahead touches, never read
+  asm volatile("" ::"v"(lds), "v"(lsa0), "v"(lsa1), "v"(lscrap) : "memory");
 
   // ---- work item: (tile, column block); XCD-contiguous ranges keep a tile's
   // column blocks (which share its A rows) and an expert's tiles (which share
@@ -285,6 +295,7 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
       const int64_t arow = a_row(p, gv, m < m_end ? m : m0);  // rows past the tile reuse a valid row
       aoff[i] = (uint32_t)(arow * p.lda_b + 16 * swz(row, lane & 7));
     }
+    const int S = p.stages;
     // activation scales: waves 0 .. MT-1 copy the scales of rows 64 wave + lane
     const bool scale_wave = kScaled && wave < MT;
     uint32_t soff = 0;
@@ -294,6 +305,22 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
     }
     auto stage_ptr = [&](int u) -> uint8_t* { return lds + u * (kRows * 128); };
     auto scale_ptr = [&](int u) -> float* { return u ? lsa1 : lsa0; };
+    // Look-ahead touch (kPF > 0): with the copies of stage s each wave also
+    // reads 4 bytes of each of 64 rows' 128-byte line of stage s + kPF (waves
+    // 0-3: the weight rows, 4-7: the A rows) into a scrap LDS word, so that
+    // line is on its way into L2 well before its copy is issued. In-order
+    // completion means the copies of stage s + 2 wait for it, which leaves it
+    // two stages of time; the copies themselves then find L2 lines.
+    const uint8_t* pbase = uniform_ptr(wave_u < 4 ? ((GATEUP && wave_u >= 2) ? bb1 : bb0) : p.a);
+    uint32_t poff;
+    if (wave_u < 4) {
+      const int row = 64 * wave_u + lane;
+      if (GATEUP) poff = (uint32_t)((row % (kWBN / 2)) * p.ldw_b);
+      else poff = (uint32_t)((ncol0 + row < n_valid ? ncol0 + row : 0) * p.ldw_b);
+    } else {
+      const int m = m0 + 64 * (wave_u - 4) + lane;
+      poff = (uint32_t)(a_row(p, gv, m < m_end ? m : m0) * p.lda_b);
+    }
     auto issue = [&](int u, int s) {
       const uint32_t st = (uint32_t)(uintptr_t)stage_ptr(u);
       const int64_t off = (int64_t)s * 128;
@@ -304,6 +331,8 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
         lds_copy16_s(((GATEUP && i >= kInstB / 2) ? bb1 : bb0) + off, boff[i],
                      st + (kWBM + 8 * kWWaves * i + 8 * wave_u) * 128);
       if (scale_wave) lds_copy4_s(p.a_scales + s, soff, (uint32_t)(uintptr_t)scale_ptr(u) + 256 * wave_u);
+      if constexpr (kPF > 0)
+        lds_copy4_s(pbase + (int64_t)min(s + kPF, S - 1) * 128, poff, (uint32_t)(uintptr_t)lscrap);
     };
 
     f32x4 acc[MT][8];
@@ -369,23 +398,54 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
           }
         }
       } else if constexpr (MODE == kModeFP8) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        // Software pipeline over the column tiles: the MT products of tile j
+        // are issued before the promotion of tile j - 1's products, so the
+        // promotion FMAs never wait on a matrix-core result just issued and
+        // they overlap the next MFMAs.
+        auto bfrag = [&](int j) -> i32x8 {
           const int bj = brow(j);
           const uint8_t* bp = st + (kWBM + bj) * 128;
           const i32x4 b0 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4));
           const i32x4 b1 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1));
-          const i32x8 b8 = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-          const int wsel = (GATEUP && j >= 4) ? 1 : 0;
+          return i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        };
+        i32x8 a8[MT];
 #pragma unroll
-          for (int i = 0; i < MT; ++i) {
-            const i32x8 a8 = i32x8{fa[i][0][0], fa[i][0][1], fa[i][0][2], fa[i][0][3],
-                                   fa[i][1][0], fa[i][1][1], fa[i][1][2], fa[i][1][3]};
-            const f32x4 pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                               0, 0, 0, 0);
+        for (int i = 0; i < MT; ++i)
+          a8[i] = i32x8{fa[i][0][0], fa[i][0][1], fa[i][0][2], fa[i][0][3],
+                        fa[i][1][0], fa[i][1][1], fa[i][1][2], fa[i][1][3]};
+        f32x4 prev[MT];
+        i32x8 bnext = bfrag(0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pr[r], saw[wsel][i], acc[i][j][r]);
+        for (int j = 0; j < 8; ++j) {
+          const i32x8 b8 = bnext;
+          if (j + 1 < 8) bnext = bfrag(j + 1);
+          f32x4 cur[MT];
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+            cur[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                      0, 0, 0);
+          if (j > 0) {
+            const int wsel = (GATEUP && j - 1 >= 4) ? 1 : 0;
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[i][j - 1][r] = fmaf(prev[i][r], saw[wsel][i], acc[i][j - 1][r]);
           }
+#if DMOE_WIDE_SCHED
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // the next B fragment's LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);      // this tile's MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x002, 4 * MT, 0);  // the previous tile's promotion
+#endif
+#pragma unroll
+          for (int i = 0; i < MT; ++i) prev[i] = cur[i];
+        }
+        {
+          const int wsel = GATEUP ? 1 : 0;
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][7][r] = fmaf(prev[i][r], saw[wsel][i], acc[i][7][r]);
         }
       } else {
 #pragma unroll
@@ -409,16 +469,17 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
     // every wave has passed the barrier of stage s (so is done with stage s - 1,
     // whose buffer it refills) and lands while stage s is computed.
     __syncthreads();  // weight scales staged
-    const int S = p.stages;
     issue(0, 0);
     if (S > 1) issue(1, 1);
+    constexpr int kT = kPF > 0 ? 1 : 0;  // look-ahead loads per wave per stage
     for (int s = 0; s < S; ++s) {
       const int u = s & 1;
+      // stage s has landed once at most the loads issued after its copies are in flight
       if (s == 0 && S > 1) {
-        if (scale_wave) wait_vmcnt<kCopies + 1>();
-        else wait_vmcnt<kCopies>();
+        if (scale_wave) wait_vmcnt<kCopies + 1 + 2 * kT>();
+        else wait_vmcnt<kCopies + 2 * kT>();
       } else {
-        wait_vmcnt<0>();
+        wait_vmcnt<kT>();
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads of stage s - 1 are done
       stage_barrier();
