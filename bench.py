@@ -65,15 +65,31 @@ def shared_fused(cfg) -> bool:
     return cfg.T_s > 0 and cfg.F_s > 0 and cfg.F_s == cfg.F
 
 
-def kernel_files(stream: bool) -> list[str]:
+def gateup_kernel(cfg) -> str:
+    """The library's gate/up kernel for this workload (the same host rule as the launcher): the weight-streaming
+    kernel for at most 32 rows per expert; otherwise the two-workgroup tile kernel for FP8 (exact products) and
+    for fewer than 128 rows per expert or too few 256-row work items; the wide tile kernel for the rest."""
+    if uses_stream_kernel(cfg):
+        return "gemm_stage_kernel"
+    max_rows, e_loc = cfg.T * cfg.K, cfg.E_loc
+    x_rows = cfg.T_s if shared_fused(cfg) else 0
+    cap = -(-max_rows // 256) + e_loc + -(-x_rows // 256)
+    items = cap * (-(-cfg.F // 128))
+    if cfg.dtype == "fp8" or -(-max_rows // e_loc) < 128 or items < 1024:
+        return "gemm_tile_kernel"
+    return "gemm_wide_kernel"
+
+
+def kernel_files(kernel: str) -> list[str]:
     csrc = os.path.join(ROOT, "fp8_expert_ffn_amd", "csrc")
-    main = "gemm_stream.hip" if stream else "gemm.hip"
+    main = {"gemm_stage_kernel": "gemm_stream.hip", "gemm_tile_kernel": "gemm.hip",
+            "gemm_wide_kernel": "gemm_wide.hip"}[kernel]
     return [os.path.join(csrc, f) for f in (main, "gemm_common.h", "dmoe_device.h", "dmoe_internal.h")]
 
 
-def kernel_source_hash(stream: bool) -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in kernel_files(stream):
+    for f in kernel_files(kernel):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -376,11 +392,11 @@ def main() -> int:
         roof = {"bound": "hbm", **hbm_side, "traffic": None, "other_roof": {"bound": "mfma", **mfma_side}}
     else:
         roof = {"bound": "mfma", **mfma_side, "traffic": None, "other_roof": {"bound": "hbm", **hbm_side}}
-    stream_k = uses_stream_kernel(cfg)
-    kname = f"{'gemm_stage_kernel' if stream_k else 'gemm_tile_kernel'}<{cfg.dtype}, gate/up>"
+    kbase = gateup_kernel(cfg)
+    kname = f"{kbase}<{cfg.dtype}, gate/up>"
     roof["kernel"] = kname + (" (routed experts + shared expert as an extra group)" if shared_fused(cfg)
                               else " (routed experts)")
-    rec = traffic_record(cfg.name, kname, kernel_source_hash(stream_k))
+    rec = traffic_record(cfg.name, kname, kernel_source_hash(kbase))
     if rec is not None:
         roof["traffic"] = rec["hbm_bytes_per_launch"]
         roof["traffic_source"] = rec["summary"]

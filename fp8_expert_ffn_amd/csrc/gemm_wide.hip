@@ -35,86 +35,17 @@ constexpr int kWWaves = kWThreads / 64;
 #ifndef DMOE_WIDE_XCD_REMAP
 #define DMOE_WIDE_XCD_REMAP 1
 #endif
-// FP8 gate/up on FP8 matrix cores with the slice-amax repair (1), or on BF16
-// matrix cores with exact products (0)
-#ifndef DMOE_WIDE_GU_FP8
-#define DMOE_WIDE_GU_FP8 0
-#endif
-// look-ahead distance in stages of the L2 touch of future A and weight lines (0: none)
-#ifndef DMOE_WIDE_PF
-#define DMOE_WIDE_PF 0
-#endif
-// scheduling directives that keep the FP8 MFMA / promotion software pipeline in order
-#ifndef DMOE_WIDE_SCHED
-#define DMOE_WIDE_SCHED 0
-#endif
-constexpr int kPF = DMOE_WIDE_PF;
-
-// Relative bound used to decide whether the FP8 matrix cores' h can settle a
-// slice's BF16 amax: the largest relative difference between the slice amax
-// from FP8 MFMA products and the one from exact products, measured over the
-// 786,432 slices of the full prefill layer, was 8.7e-5; this bound is 2.9x that.
-constexpr float kAmaxTau = 2.5e-4f;
-
 __device__ __forceinline__ float bf16r(float v) { return bf16_to_f32(f32_to_bf16(v)); }
-
-// g and u of one h element from exact products (E4M3 values are exact in FP32
-// and so are their products), each 128-wide slice summed in FP32 and promoted
-// with a_scale * w_scale as in the exact-product GEMM; a wave computes one
-// element (lane j takes slices j, j + 64, ...), the slice terms are added by a
-// butterfly, so every lane returns the same h = silu(g) * u.
-__device__ float exact_h(const TileArgs& p, const GroupView& gv, int64_t arow, int wrow, const float* wsg,
-                         const float* wsu, int lane) {
-  const uint8_t* ap = p.a + arow * p.lda_b;
-  const uint8_t* gp = gv.w0 + (int64_t)wrow * p.ldw_b;
-  const uint8_t* up = gv.w1 + (int64_t)wrow * p.ldw_b;
-  float cg = 0.f, cu = 0.f;
-  for (int j = lane; j < p.nKb; j += 64) {
-    float sg = 0.f, su = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const i32x4 a = *reinterpret_cast<const i32x4*>(ap + j * 128 + 16 * q);
-      const i32x4 g = *reinterpret_cast<const i32x4*>(gp + j * 128 + 16 * q);
-      const i32x4 u = *reinterpret_cast<const i32x4*>(up + j * 128 + 16 * q);
-      typedef float f32x2 __attribute__((ext_vector_type(2)));
-      auto mac2 = [&](f32x2 af, f32x2 gf, f32x2 uf) {
-        sg = fmaf(af[0], gf[0], sg);
-        sg = fmaf(af[1], gf[1], sg);
-        su = fmaf(af[0], uf[0], su);
-        su = fmaf(af[1], uf[1], su);
-      };
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        mac2(__builtin_amdgcn_cvt_pk_f32_fp8(a[w], false), __builtin_amdgcn_cvt_pk_f32_fp8(g[w], false),
-             __builtin_amdgcn_cvt_pk_f32_fp8(u[w], false));
-        mac2(__builtin_amdgcn_cvt_pk_f32_fp8(a[w], true), __builtin_amdgcn_cvt_pk_f32_fp8(g[w], true),
-             __builtin_amdgcn_cvt_pk_f32_fp8(u[w], true));
-      }
-    }
-    const float sa = p.a_scales[arow * p.ldas + j];
-    cg = fmaf(sg, sa * wsg[j], cg);
-    cu = fmaf(su, sa * wsu[j], cu);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    cg += __shfl_xor(cg, off);
-    cu += __shfl_xor(cu, off);
-  }
-  return silu(cg) * cu;
-}
 
 // Epilogue of the FP8 gate/up launch in the layer: h = silu(g) * u goes to LDS
 // (FP32, [256 rows][128 columns], 16-byte units XOR-swizzled by row), then two
 // threads per row round it to BF16 and quantise the row's 128-column slice with
 // the activation rule (amax over the BF16 values, s = f32(amax / 448), codes by
-// round-to-nearest-even), as dmoe_quant_act does for a BF16 h. With FP8 matrix
-// cores (REPAIR) a row whose BF16 amax the kAmaxTau bound leaves undecided gets
-// every element that could be its largest recomputed from exact products first,
-// so the slice scale is the one exact products give.
-template <bool REPAIR, bool QUANT, int MT>
-__device__ __forceinline__ void quantise_h_epilogue(const TileArgs& p, const GroupView& gv, const f32x4 (&acc)[MT][8],
-                                                    float* hx, int m0, int m_end, int ncol0, int wm, int wn, int lane,
-                                                    int r16, int g4, const float* wsg, const float* wsu) {
+// round-to-nearest-even), as dmoe_quant_act does for a BF16 h, and write the
+// codes as 64-byte runs.
+template <int MT>
+__device__ __forceinline__ void quantise_h_epilogue(const TileArgs& p, const f32x4 (&acc)[MT][8], float* hx, int m0,
+                                                    int m_end, int ncol0, int wm, int wn, int r16, int g4) {
   auto unit = [&](int row, int u) -> f32x4* { return reinterpret_cast<f32x4*>(hx + row * 128) + (u ^ (row & 31)); };
   __builtin_amdgcn_s_waitcnt(0xc07f);
   stage_barrier();  // every wave is done reading the ring
@@ -133,70 +64,18 @@ __device__ __forceinline__ void quantise_h_epilogue(const TileArgs& p, const Gro
   const int row = (int)(threadIdx.x >> 1), half = (int)(threadIdx.x & 1);
   const bool valid = m0 + row < m_end;
   float v[64];
-  auto load = [&]() {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const f32x4 t = *unit(row, 16 * half + k);
+  for (int k = 0; k < 16; ++k) {
+    const f32x4 t = *unit(row, 16 * half + k);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[4 * k + r] = t[r];
-    }
-  };
-  auto row_max = [&]() {
-    float m = 0.f;
-#pragma unroll
-    for (int k = 0; k < 64; ++k) m = fmaxf(m, fabsf(v[k]));
-    return fmaxf(m, __shfl_xor(m, 1));
-  };
-  load();
-  float mx = row_max();
-  if constexpr (REPAIR) {
-    // BF16 amax undecided within the bound: both ends of [mx (1 - tau), mx (1 + tau)] must round alike
-    const bool unc = valid && bf16r(mx * (1.f - kAmaxTau)) != bf16r(mx * (1.f + kAmaxTau));
-    uint64_t todo = __ballot(unc && half == 0);
-    if (todo) {
-      while (todo) {
-        const int l0 = __ffsll((unsigned long long)todo) - 1;
-        todo &= todo - 1;
-        const int rrow = __shfl(row, l0);
-        const float thr = __shfl(mx, l0) * ((1.f - kAmaxTau) / (1.f + kAmaxTau));
-        // columns whose value could be the row's largest
-        uint64_t mine = 0;
-        if (row == rrow) {
-#pragma unroll
-          for (int k = 0; k < 64; ++k)
-            if (fabsf(v[k]) >= thr) mine |= 1ull << k;
-        }
-        const uint64_t c0 = shfl_u64(mine, l0), c1 = shfl_u64(mine, l0 + 1);
-        const int64_t arow = a_row(p, gv, m0 + rrow);
-        for (int hf = 0; hf < 2; ++hf) {
-          uint64_t c = hf ? c1 : c0;
-          while (c) {
-            const int k = __ffsll((unsigned long long)c) - 1;
-            c &= c - 1;
-            const int col = 64 * hf + k;
-            const float h = exact_h(p, gv, arow, ncol0 + col, wsg, wsu, lane);
-            if (lane == 0) hx[rrow * 128 + 4 * ((col >> 2) ^ (rrow & 31)) + (col & 3)] = h;
-          }
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are done before its lanes reload
-      load();
-      mx = row_max();
-    }
+    for (int r = 0; r < 4; ++r) v[4 * k + r] = t[r];
   }
+  float mx = 0.f;
+#pragma unroll
+  for (int k = 0; k < 64; ++k) mx = fmaxf(mx, fabsf(v[k]));
+  mx = fmaxf(mx, __shfl_xor(mx, 1));  // the row's other half
   if (!valid) return;
   const int m = m0 + row;
-  if constexpr (!QUANT) {
-    // BF16 h (the standalone gate/up call): the values a fused quantisation would have used
-    uint16_t* hrow = p.out + (int64_t)m * p.ldo + ncol0 + 64 * half;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const float* q = v + 8 * b;
-      *reinterpret_cast<uint4*>(hrow + 8 * b) = make_uint4(pack_bf16x2(q[0], q[1]), pack_bf16x2(q[2], q[3]),
-                                                           pack_bf16x2(q[4], q[5]), pack_bf16x2(q[6], q[7]));
-    }
-    return;
-  }
   const float s = div_rn(bf16r(mx), 448.f);
   uint8_t* qrow = p.out_q + (int64_t)m * p.ldo + ncol0 + 64 * half;
   const ScaleDiv d = make_scale_div(s != 0.f ? s : 1.f);
@@ -223,13 +102,13 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
   static_assert(kInstB * 8 * kWWaves == kWBN, "copy split");
   static_assert(!QH || (GATEUP && MODE != kModeBF16), "h quantisation belongs to the FP8 gate/up epilogue");
   static_assert(GATEUP || MODE != kModeFP8X, "the exact-product mode serves gate/up only");
+  static_assert(!GATEUP || MODE != kModeFP8, "FP8 gate/up takes exact products (BF16 matrix cores)");
   // the 2-stage ring; after the K loop the FP8 gate/up epilogue reuses it for h
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kRows * 128];
   __shared__ __attribute__((aligned(256))) float lsa0[kWBM];
   __shared__ __attribute__((aligned(256))) float lsa1[kWBM];
   __shared__ float lsw[2][kMaxSlices];
-  __shared__ __attribute__((aligned(256))) float lscrap[64];  // target of the look-ahead touches, never read
-  asm volatile("" ::"v"(lds), "v"(lsa0), "v"(lsa1), "v"(lscrap) : "memory");
+  asm volatile("" ::"v"(lds), "v"(lsa0), "v"(lsa1) : "memory");
 
   // ---- work item: (tile, column block); XCD-contiguous ranges keep a tile's
   // column blocks (which share its A rows) and an expert's tiles (which share
@@ -305,22 +184,6 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
     }
     auto stage_ptr = [&](int u) -> uint8_t* { return lds + u * (kRows * 128); };
     auto scale_ptr = [&](int u) -> float* { return u ? lsa1 : lsa0; };
-    // Look-ahead touch (kPF > 0): with the copies of stage s each wave also
-    // reads 4 bytes of each of 64 rows' 128-byte line of stage s + kPF (waves
-    // 0-3: the weight rows, 4-7: the A rows) into a scrap LDS word, so that
-    // line is on its way into L2 well before its copy is issued. In-order
-    // completion means the copies of stage s + 2 wait for it, which leaves it
-    // two stages of time; the copies themselves then find L2 lines.
-    const uint8_t* pbase = uniform_ptr(wave_u < 4 ? ((GATEUP && wave_u >= 2) ? bb1 : bb0) : p.a);
-    uint32_t poff;
-    if (wave_u < 4) {
-      const int row = 64 * wave_u + lane;
-      if (GATEUP) poff = (uint32_t)((row % (kWBN / 2)) * p.ldw_b);
-      else poff = (uint32_t)((ncol0 + row < n_valid ? ncol0 + row : 0) * p.ldw_b);
-    } else {
-      const int m = m0 + 64 * (wave_u - 4) + lane;
-      poff = (uint32_t)(a_row(p, gv, m < m_end ? m : m0) * p.lda_b);
-    }
     auto issue = [&](int u, int s) {
       const uint32_t st = (uint32_t)(uintptr_t)stage_ptr(u);
       const int64_t off = (int64_t)s * 128;
@@ -331,8 +194,6 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
         lds_copy16_s(((GATEUP && i >= kInstB / 2) ? bb1 : bb0) + off, boff[i],
                      st + (kWBM + 8 * kWWaves * i + 8 * wave_u) * 128);
       if (scale_wave) lds_copy4_s(p.a_scales + s, soff, (uint32_t)(uintptr_t)scale_ptr(u) + 256 * wave_u);
-      if constexpr (kPF > 0)
-        lds_copy4_s(pbase + (int64_t)min(s + kPF, S - 1) * 128, poff, (uint32_t)(uintptr_t)lscrap);
     };
 
     f32x4 acc[MT][8];
@@ -432,11 +293,6 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
 #pragma unroll
               for (int r = 0; r < 4; ++r) acc[i][j - 1][r] = fmaf(prev[i][r], saw[wsel][i], acc[i][j - 1][r]);
           }
-#if DMOE_WIDE_SCHED
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // the next B fragment's LDS reads
-          __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);      // this tile's MFMAs
-          __builtin_amdgcn_sched_group_barrier(0x002, 4 * MT, 0);  // the previous tile's promotion
-#endif
 #pragma unroll
           for (int i = 0; i < MT; ++i) prev[i] = cur[i];
         }
@@ -471,15 +327,14 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
     __syncthreads();  // weight scales staged
     issue(0, 0);
     if (S > 1) issue(1, 1);
-    constexpr int kT = kPF > 0 ? 1 : 0;  // look-ahead loads per wave per stage
     for (int s = 0; s < S; ++s) {
       const int u = s & 1;
-      // stage s has landed once at most the loads issued after its copies are in flight
+      // stage s has landed once at most the copies issued after it (stage 1, at s = 0) are in flight
       if (s == 0 && S > 1) {
-        if (scale_wave) wait_vmcnt<kCopies + 1 + 2 * kT>();
-        else wait_vmcnt<kCopies + 2 * kT>();
+        if (scale_wave) wait_vmcnt<kCopies + 1>();
+        else wait_vmcnt<kCopies>();
       } else {
-        wait_vmcnt<kT>();
+        wait_vmcnt<0>();
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads of stage s - 1 are done
       stage_barrier();
@@ -491,10 +346,8 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
     if constexpr (GATEUP) {
       // h columns of this lane: ncol0 + 64 wn + 16 jj + 4 g4 + r (jj = 0..3)
       const int hcol0 = ncol0 + 64 * wn + 4 * g4;
-      if constexpr (QH || MODE == kModeFP8) {
-        // staged through LDS: h quantised (QH), and with FP8 matrix cores the undecided slice amax repaired
-        quantise_h_epilogue<MODE == kModeFP8, QH, MT>(p, gv, acc, reinterpret_cast<float*>(lds), m0, m_end, ncol0,
-                                                       wm, wn, lane, r16, g4, lsw[0], lsw[1]);
+      if constexpr (QH) {
+        quantise_h_epilogue<MT>(p, acc, reinterpret_cast<float*>(lds), m0, m_end, ncol0, wm, wn, r16, g4);
       } else {
         const bool wide = (p.ldo & 3) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 7) == 0;
 #pragma unroll
@@ -558,9 +411,8 @@ hipError_t launch_gemm_wide(const TileArgs& p, int dtype, bool gateup, int npad,
   const bool qh = p.out_q != nullptr;
   if (dtype == DMOE_FP8_E4M3) {
     if (gateup) {
-      constexpr int kGU = DMOE_WIDE_GU_FP8 ? kModeFP8 : kModeFP8X;
-      if (qh) gemm_wide_kernel<kGU, true, true><<<grid, kWThreads, 0, stream>>>(p, nNB, npad);
-      else gemm_wide_kernel<kGU, true, false><<<grid, kWThreads, 0, stream>>>(p, nNB, npad);
+      if (qh) gemm_wide_kernel<kModeFP8X, true, true><<<grid, kWThreads, 0, stream>>>(p, nNB, npad);
+      else gemm_wide_kernel<kModeFP8X, true, false><<<grid, kWThreads, 0, stream>>>(p, nNB, npad);
     } else {
       gemm_wide_kernel<kModeFP8, false, false><<<grid, kWThreads, 0, stream>>>(p, nNB, npad);
     }
