@@ -54,30 +54,9 @@ def build_layer(cfg, dev):
     return layer
 
 
-def uses_stream_kernel(cfg) -> bool:
-    """The library's choice for the grouped GEMMs: the weight-streaming kernel when the host bound on rows per
-    local expert, ceil(T*K / E_loc), is at most 32; tile GEMM otherwise."""
-    return -(-cfg.T * cfg.K // cfg.E_loc) <= 32
-
-
 def shared_fused(cfg) -> bool:
     """The shared expert runs inside the routed launches when it has the routed width."""
     return cfg.T_s > 0 and cfg.F_s > 0 and cfg.F_s == cfg.F
-
-
-def gateup_kernel(cfg) -> str:
-    """The library's gate/up kernel for this workload (the same host rule as the launcher): the weight-streaming
-    kernel for at most 32 rows per expert; otherwise the two-workgroup tile kernel for FP8 (exact products) and
-    for fewer than 128 rows per expert or too few 256-row work items; the wide tile kernel for the rest."""
-    if uses_stream_kernel(cfg):
-        return "gemm_stage_kernel"
-    max_rows, e_loc = cfg.T * cfg.K, cfg.E_loc
-    x_rows = cfg.T_s if shared_fused(cfg) else 0
-    cap = -(-max_rows // 256) + e_loc + -(-x_rows // 256)
-    items = cap * (-(-cfg.F // 128))
-    if cfg.dtype == "fp8" or -(-max_rows // e_loc) < 128 or items < 1024:
-        return "gemm_tile_kernel"
-    return "gemm_wide_kernel"
 
 
 def kernel_files(kernel: str) -> list[str]:
@@ -277,6 +256,7 @@ def main() -> int:
     import torch
     import synth
     import fp8_expert_ffn_amd as dm
+    from fp8_expert_ffn_amd import _lib as dml
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -398,7 +378,7 @@ def main() -> int:
         roof = {"bound": "hbm", **hbm_side, "traffic": None, "other_roof": {"bound": "mfma", **mfma_side}}
     else:
         roof = {"bound": "mfma", **mfma_side, "traffic": None, "other_roof": {"bound": "hbm", **hbm_side}}
-    kbase = gateup_kernel(cfg)
+    kbase = dml.dmoe_forward_gateup_kernel(d)  # the launcher's own choice for this layer
     kname = f"{kbase}<{cfg.dtype}, gate/up>"
     roof["kernel"] = kname + (" (routed experts + shared expert as an extra group)" if shared_fused(cfg)
                               else " (routed experts)")

@@ -500,6 +500,12 @@ size_t dmoe_forward_ws_bytes(const dmoe_layer_desc* desc) {
   return (size_t)fwd_layout(desc).total;
 }
 
+const char* dmoe_forward_gateup_kernel(const dmoe_layer_desc* desc) {
+  if (check_desc(desc) != DMOE_OK) return nullptr;
+  const int mcap = desc->T * desc->K;
+  return gemm_gateup_kernel_name(desc->dtype, mcap, desc->E_loc, fuse_shared(desc) ? desc->T_s : 0, desc->F);
+}
+
 int64_t dmoe_forward_ws_offset(const dmoe_layer_desc* desc, int32_t which) {
   if (check_desc(desc) != DMOE_OK || which < 0 || which > W_S) return -1;
   return fwd_layout(desc).off[which];
@@ -641,7 +647,7 @@ static dmoe_status forward_impl(const dmoe_layer_desc* d, const dmoe_layer_ptrs*
     g1.xws1 = p->sws_up;
   }
   // FP8 with the wide tile kernel: h is quantised in the gate/up epilogue
-  const bool fused_quant = fp8 && gemm_fuses_h_quant(mcap, d->E_loc);
+  const bool fused_quant = fp8 && gemm_fuses_h_quant(mcap, d->E_loc, xrows, d->F);
   if (fused_quant) {
     g1.out_q = at(W_HQ);
     g1.out_s = reinterpret_cast<float*>(at(W_HS));

@@ -107,7 +107,11 @@ hipError_t launch_schedule(const int32_t* offsets, int E_loc, int max_rows, int 
 // true when launch_gemm_* picks the weight-streaming kernel (it needs no tile schedule)
 bool gemm_uses_stream(int max_rows, int E_loc);
 // true when the FP8 gate/up launch can quantise h in its epilogue (GemmArgs.out_q)
-bool gemm_fuses_h_quant(int max_rows, int E_loc);
+// true when the FP8 gate/up launch of this shape runs on the wide kernel with h
+// quantised in its epilogue (build option DMOE_WIDE_GU); N = output columns (F)
+bool gemm_fuses_h_quant(int max_rows, int E_loc, int extra_rows, int N);
+// name of the kernel a gate/up launch of this shape runs (the launcher's rule)
+const char* gemm_gateup_kernel_name(int dtype, int max_rows, int E_loc, int extra_rows, int N);
 hipError_t launch_gemm_gateup(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_fill_offsets(int32_t* offsets, int rows, hipStream_t stream);

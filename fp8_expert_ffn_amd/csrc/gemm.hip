@@ -489,10 +489,14 @@ hipError_t launch_fill_offsets(int32_t* offsets, int rows, hipStream_t stream) {
 // two workgroups per CU) for the FP8 gate/up projection with exact products,
 // where the two independent workgroups per CU overlap one's E4M3 -> BF16
 // conversions with the other's matrix-core work (measured faster there: prefill
-// gate/up 2.58 vs 2.88 ms). DMOE_WIDE_GU = 1 puts FP8 gate/up on the wide kernel
-// too, with h quantised in its epilogue.
+// gate/up 2.58 vs 2.88 ms). FP8 gate/up moves to the wide kernel, with h
+// quantised in its epilogue, when the host bound on rows per expert reaches
+// DMOE_WIDE_GU (0: never): with many rows per expert its 256-row tiles halve
+// the bytes staged per FLOP and the saved quantise launch pays (EP share, 4096
+// rows per expert: layer 5.59 -> 5.24 ms; dense FFN 1.55 -> 1.48 ms; the vision
+// layer's 512 rows per expert gain nothing, prefill's 256 lose).
 #ifndef DMOE_WIDE_GU
-#define DMOE_WIDE_GU 0
+#define DMOE_WIDE_GU 1024
 #endif
 // The GEMM workspace holds two tile schedules, one per tile height:
 // [tiles of 128 rows][count] [tiles of 256 rows][count].
@@ -508,7 +512,8 @@ static int64_t sched_bytes(int bm, int max_rows, int E_loc, int extra_rows) {
 // leave most of each tile empty) and enough work items to fill the CUs several
 // times over (a dense 4096-row layer's down projection has only 340).
 static bool use_wide(int dtype, bool gateup, int max_rows, int E_loc, int extra_rows, int64_t npad) {
-  if (gateup && dtype == DMOE_FP8_E4M3 && !DMOE_WIDE_GU) return false;
+  if (gateup && dtype == DMOE_FP8_E4M3 && (DMOE_WIDE_GU <= 0 || ceil_div(max_rows, E_loc) < DMOE_WIDE_GU))
+    return false;
   const int64_t col_blocks = gateup ? npad / 128 : ceil_div(npad, 256);
   const int64_t items = (int64_t)tile_cap(kWideBM, max_rows, E_loc, extra_rows) * col_blocks;
   return ceil_div(max_rows, E_loc) >= 128 && items >= 1024;
@@ -545,8 +550,15 @@ hipError_t launch_schedule(const int32_t* offsets, int E_loc, int max_rows, int 
 
 bool gemm_uses_stream(int max_rows, int E_loc) { return ceil_div(max_rows, E_loc) <= 32; }
 
-bool gemm_fuses_h_quant(int max_rows, int E_loc) {
-  return DMOE_WIDE_GU && !gemm_uses_stream(max_rows, E_loc);
+const char* gemm_gateup_kernel_name(int dtype, int max_rows, int E_loc, int extra_rows, int N) {
+  if (gemm_uses_stream(max_rows, E_loc)) return "gemm_stage_kernel";
+  return use_wide(dtype, true, max_rows, E_loc, extra_rows, round_up(N, 128)) ? "gemm_wide_kernel"
+                                                                               : "gemm_tile_kernel";
+}
+
+bool gemm_fuses_h_quant(int max_rows, int E_loc, int extra_rows, int N) {
+  return DMOE_WIDE_GU > 0 && !gemm_uses_stream(max_rows, E_loc) &&
+         use_wide(DMOE_FP8_E4M3, true, max_rows, E_loc, extra_rows, round_up(N, 128));
 }
 
 static hipError_t launch_gemm(const GemmArgs& g, bool gateup, hipStream_t stream) {
@@ -594,6 +606,8 @@ static hipError_t launch_gemm(const GemmArgs& g, bool gateup, hipStream_t stream
   p.out_q = g.out_q;
   p.out_s = g.out_s;
   p.ld_s = g.ld_s;
+  // only the wide kernel quantises h in its epilogue (gemm_fuses_h_quant decides both)
+  if (g.out_q && (use_stream || !wide || !gateup || g.dtype != DMOE_FP8_E4M3)) return hipErrorInvalidValue;
   // Few rows per expert on average: stream the weights (the tile schedule is not used).
   if (use_stream) {
     p.x_chunk = per_expert <= 16 ? 16 : 32;

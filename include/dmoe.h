@@ -383,9 +383,19 @@ dmoe_status dmoe_forward_timed(const dmoe_layer_desc* desc, const dmoe_layer_ptr
  * Views into the forward workspace, for inspection after dmoe_forward (host
  * byte offsets from ws; -1 if the buffer does not exist for this desc):
  * 0 offsets, 1 row_token, 2 row_slot, 3 token_row, 4 x codes, 5 x scales,
- * 6 h (BF16), 7 h codes, 8 h scales, 9 o, 10 shared output.
+ * 6 h (BF16; not written for FP8 when the gate/up launch quantises h itself,
+ * see dmoe_forward_gateup_kernel), 7 h codes, 8 h scales, 9 o, 10 shared output.
  */
 int64_t dmoe_forward_ws_offset(const dmoe_layer_desc* desc, int32_t which);
+
+/*
+ * Name of the GEMM kernel that the layer's gate/up launch runs for this desc:
+ * "gemm_stage_kernel" (weight streaming, few rows per expert), "gemm_tile_kernel"
+ * or "gemm_wide_kernel" (a static string; NULL for an invalid desc). For
+ * profiling and reports; no GPU work. With FP8 the wide kernel quantises h in
+ * its epilogue, so workspace view 6 (BF16 h) is then not written.
+ */
+const char* dmoe_forward_gateup_kernel(const dmoe_layer_desc* desc);
 
 /*
  * dmoe_forward without a caller workspace, for callers that cannot allocate

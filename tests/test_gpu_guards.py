@@ -23,9 +23,15 @@ from fp8_expert_ffn_amd import _lib as L  # noqa: E402
 SENT = 0xA5
 
 CASES = {
-    # tile GEMMs (the wide kernel), FP8 h quantised in the gate/up epilogue
+    # tile GEMMs: the two-workgroup kernel for gate/up, separate FP8 h quantisation
     "tile_fp8": synth.LayerConfig("guard_tile_fp8", T=700, H=512, F=200, F_s=200, E=16, E_loc=16, e0=0, K=4,
                                   dtype="fp8", T_s=300, logits="uniform"),
+    # FP8 gate/up on the wide kernel with h quantised in its epilogue (1024 rows per expert by the host bound),
+    # with all pairs local and as an EP share
+    "wide_fp8": synth.LayerConfig("guard_wide_fp8", T=2048, H=256, F=3200, F_s=3200, E=8, E_loc=8, e0=0, K=4,
+                                  dtype="fp8", T_s=300, logits="uniform"),
+    "wide_ep_fp8": synth.LayerConfig("guard_wide_ep_fp8", T=1024, H=256, F=3200, F_s=3200, E=64, E_loc=8, e0=8,
+                                     K=8, dtype="fp8", T_s=100, logits="zipf"),
     # an EP share: most pairs are not local, so M is far below T*K
     "ep_fp8": synth.LayerConfig("guard_ep_fp8", T=900, H=512, F=256, F_s=256, E=64, E_loc=8, e0=8, K=8,
                                 dtype="fp8", T_s=100, logits="zipf"),

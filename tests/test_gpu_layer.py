@@ -90,6 +90,13 @@ CASES = {
                                         dtype="fp8", T_s=700, logits="router"),
     "wide_tiles_bf16": synth.LayerConfig("wide_tiles_bf16", T=1500, H=768, F=256, F_s=256, E=6, E_loc=6, e0=0,
                                          K=2, dtype="bf16", T_s=1500, logits="uniform"),
+    # FP8 gate/up on the wide tile GEMM with h quantised in its epilogue (at least 1024 rows per expert by the
+    # host bound and 1024 work items): uniform routing with a ragged shared-expert tail, and a Zipf-skewed EP
+    # share whose experts range from a few to thousands of rows
+    "wide_gateup_fp8": synth.LayerConfig("wide_gateup_fp8", T=4096, H=256, F=3200, F_s=3200, E=8, E_loc=8, e0=0,
+                                         K=2, dtype="fp8", T_s=300, logits="uniform"),
+    "wide_gateup_ep_fp8": synth.LayerConfig("wide_gateup_ep", T=2048, H=256, F=1920, F_s=1920, E=64, E_loc=8,
+                                            e0=0, K=8, dtype="fp8", T_s=200, logits="zipf"),
     "rows_257_fp8": synth.LayerConfig("rows_257_fp8", T=257, H=512, F=256, F_s=0, E=1, E_loc=1, e0=0, K=1,
                                       dtype="fp8", T_s=0, logits="single"),
     "rows_513_bf16": synth.LayerConfig("rows_513_bf16", T=513, H=384, F=128, F_s=128, E=1, E_loc=1, e0=0, K=1,
