@@ -300,34 +300,54 @@ __global__ __launch_bounds__(128 * WN, NT == 4 ? DMOE_TILE_WAVES_PER_EU : 1) voi
         }
       }
       if constexpr (MODE == kModeFP8X) {
-        // exact products: codes -> BF16, four 16x16x32 MFMAs per 128-wide slice
+        // exact products: codes -> BF16, four 16x16x32 MFMAs per 128-wide slice,
+        // software-pipelined over the column tiles: tile j + 1's weight fragment is
+        // converted and tile j - 1's sums promoted between tile j's MFMAs, so that
+        // the VALU work never waits on a matrix-core result just issued (measured:
+        // prefill gate/up 2.60 -> 2.55 ms)
         i32x4 a16[MT][4];
   #pragma unroll
         for (int i = 0; i < MT; ++i) {
           e4m3x16_to_bf16(fa[i][0], a16[i][0], a16[i][1]);
           e4m3x16_to_bf16(fa[i][1], a16[i][2], a16[i][3]);
         }
-  #pragma unroll
-        for (int j = 0; j < NT; ++j) {
+        auto bconv = [&](int j, i32x4 (&b16)[4]) {
           const int bj = brow(j);
           const uint8_t* bp = st + (kBM + bj) * 128;
-          const i32x4 b0 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4));
-          const i32x4 b1 = *reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1));
-          i32x4 b16[4];
-          e4m3x16_to_bf16(b0, b16[0], b16[1]);
-          e4m3x16_to_bf16(b1, b16[2], b16[3]);
+          e4m3x16_to_bf16(*reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4)), b16[0], b16[1]);
+          e4m3x16_to_bf16(*reinterpret_cast<const i32x4*>(bp + 16 * swz(bj, 2 * g4 + 1)), b16[2], b16[3]);
+        };
+        auto promote = [&](int j, const f32x4 (&sums)[MT]) {
           const int wsel = (GATEUP && j >= NH) ? 1 : 0;
   #pragma unroll
+          for (int i = 0; i < MT; ++i)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sums[i][r], saw[wsel][i], acc[i][j][r]);
+        };
+        i32x4 bcur[4], bnext[4];
+        bconv(0, bcur);
+        f32x4 prev[MT];
+  #pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          if (j + 1 < NT) bconv(j + 1, bnext);
+          f32x4 cur[MT];
+  #pragma unroll
           for (int i = 0; i < MT; ++i) {
-            f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+            cur[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
             for (int k4 = 0; k4 < 4; ++k4)
-              part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b16[k4]),
-                                                             __builtin_bit_cast(bf16x8, a16[i][k4]), part, 0, 0, 0);
+              cur[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bcur[k4]),
+                                                               __builtin_bit_cast(bf16x8, a16[i][k4]), cur[i], 0, 0, 0);
+          }
+          if (j > 0) promote(j - 1, prev);
   #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[r], saw[wsel][i], acc[i][j][r]);
+          for (int i = 0; i < MT; ++i) prev[i] = cur[i];
+          if (j + 1 < NT) {
+  #pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) bcur[k4] = bnext[k4];
           }
         }
+        promote(NT - 1, prev);
       } else if constexpr (MODE == kModeFP8) {
   #pragma unroll
         for (int j = 0; j < NT; ++j) {
