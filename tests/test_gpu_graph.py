@@ -27,6 +27,9 @@ CASES = {
     # tile kernels with the device-side schedule, FP8 quantisation of x and h
     "prefill_small_fp8": synth.LayerConfig("prefill_small", T=600, H=512, F=256, F_s=256, E=16, E_loc=16, e0=0,
                                            K=4, dtype="fp8", T_s=600, logits="router"),
+    # FP8 gate/up on the wide tile kernel with h quantised in its epilogue (1024 rows per expert by the host bound)
+    "wide_gateup_fp8": synth.LayerConfig("wide_gateup_fp8", T=2048, H=256, F=3200, F_s=3200, E=8, E_loc=8, e0=0,
+                                         K=4, dtype="fp8", T_s=300, logits="router"),
     # the full verify batches (workloads verify_bf16 and verify_fp8)
     "verify_bf16": synth.config(8),
     "verify_fp8": synth.config(9),
