@@ -42,6 +42,11 @@ Readings where the pages are silent (each also listed in the design notes):
   that BF16 h is quantised like an activation); each expert output o is
   rounded to BF16; the layer output y is rounded to BF16 once, after the
   weighted sum of the routed outputs plus the shared output.
+* Where an expert output's exact value lies on a BF16 rounding midpoint within
+  float32 precision (2^-18 of its magnitude), both neighbours are correct
+  roundings of it; ``rounding_allowance`` gives, per output element, what the
+  other choice moves y by (weight x spacing), so that a comparison can accept
+  either.
 
 Functions marked "parity pinned" are checked in the CPU test suite against
 the format definition, library routines, closed forms or brute force.
@@ -58,6 +63,7 @@ __all__ = [
     "E4M3_MAX", "e4m3_values", "e4m3_encode", "bf16_to_f64", "bf16_round",
     "quantize_act", "quantize_weight_blocks", "dequantize_act", "dequantize_weight_blocks",
     "router_logits", "route", "sigmoid_scores", "route_sigmoid", "permute", "swiglu_expert", "combine",
+    "bf16_spacing", "bf16_midpoint_straddle", "rounding_allowance",
     "OracleResult", "moe_forward", "moe_forward_loops",
 ]
 
@@ -352,6 +358,41 @@ def swiglu_expert(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
     return bf16_round(o) if rounded else o
 
 
+def bf16_spacing(v: np.ndarray) -> np.ndarray:
+    """Distance between the two bfloat16 values that bracket |v| (8 significant bits: 2^(floor(log2|v|) - 7))."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    return 2.0 ** (np.floor(np.log2(np.where(a > 0, a, 1.0))) - 7)
+
+
+def bf16_midpoint_straddle(v: np.ndarray, rel: float = 2.0 ** -18) -> np.ndarray:
+    """True where the exact value v lies within rel * |v| of a midpoint between two adjacent bfloat16 values.
+
+    A sum of thousands of products carried out in float32 (or on matrix cores with float32 accumulation) is
+    only known to about that relative precision, so such a value can legitimately be rounded to either of
+    its two bfloat16 neighbours.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    u = bf16_spacing(v)
+    q = a / u
+    dist = np.abs(q - np.floor(q) - 0.5) * u
+    return (a > 0) & (dist <= rel * a)
+
+
+def rounding_allowance(o_exact: np.ndarray, token_row: np.ndarray, w: np.ndarray, s_exact: np.ndarray | None,
+                       t_s: int) -> np.ndarray:
+    """Per output element: sum over the routed pairs (and the shared expert) of |weight| x the bfloat16
+    spacing of those expert outputs whose exact value straddles a rounding midpoint (bf16_midpoint_straddle).
+
+    The layer rounds every expert output to bfloat16 before the weighted sum; where the exact value sits on a
+    midpoint within float32 precision, either neighbour is a correct rounding, and the two choices move y by
+    the weight times the spacing. Elements far from a midpoint get no allowance.
+    """
+    oa = np.where(bf16_midpoint_straddle(o_exact), bf16_spacing(o_exact), 0.0)
+    sa = None if s_exact is None else np.where(bf16_midpoint_straddle(s_exact), bf16_spacing(s_exact), 0.0)
+    return combine(oa, token_row, np.abs(np.asarray(w, dtype=np.float64)), sa, t_s, rounded=False)
+
+
 def combine(o: np.ndarray, token_row: np.ndarray, w: np.ndarray, s: np.ndarray | None, t_s: int,
             rounded: bool = True) -> np.ndarray:
     """y[t] = bf16( sum_k w[t,k] * o[token_row[t,k]] + (t < T_s ? s[t] : 0) ), summed in float64.
@@ -385,6 +426,7 @@ class OracleResult:
     x_scales: np.ndarray | None
     y: np.ndarray               # [n, H] float64 (bfloat16 values)
     y_sum: np.ndarray           # [n, H] float64: the combine's sum before its BF16 rounding
+    y_allow: np.ndarray | None = None  # [n, H] float64: rounding_allowance of the expert outputs
 
 
 def _expert_weights(cfg, weights: Callable, e: int, fp8: bool):
@@ -433,20 +475,22 @@ def moe_forward(cfg, x_bits: np.ndarray, weights: Callable, w_r: np.ndarray | No
     else:
         xq = xs = None
         a_all = x
-    o = np.zeros((int(offsets[-1]), cfg.H), dtype=np.float64)
+    o_ex = np.zeros((int(offsets[-1]), cfg.H), dtype=np.float64)  # expert outputs before their BF16 rounding
     for el in range(cfg.E_loc):
         r0, r1 = int(offsets[el]), int(offsets[el + 1])
         if r1 == r0:
             continue
         wg, wu, wd = _expert_weights(cfg, weights, cfg.e0 + el, fp8)
-        o[r0:r1] = swiglu_expert(a_all[row_token[r0:r1]], wg, wu, wd, fp8)
+        o_ex[r0:r1] = swiglu_expert(a_all[row_token[r0:r1]], wg, wu, wd, fp8, rounded=False)
     shared_rows = tok < cfg.T_s
-    s = np.zeros((tok.size, cfg.H), dtype=np.float64)
+    s_ex = np.zeros((tok.size, cfg.H), dtype=np.float64)
     if shared_rows.any():
         wg, wu, wd = _expert_weights(cfg, weights, -1, fp8)
-        s[shared_rows] = swiglu_expert(a_all[shared_rows], wg, wu, wd, fp8)
-    y_sum = combine(o, token_row, w, s, tok.size, rounded=False)  # rows of s past T_s are zero
-    return OracleResult(tok, L, ids, w, xq, xs, bf16_round(y_sum), y_sum)
+        s_ex[shared_rows] = swiglu_expert(a_all[shared_rows], wg, wu, wd, fp8, rounded=False)
+    # rows of s past T_s are zero
+    y_sum = combine(bf16_round(o_ex), token_row, w, bf16_round(s_ex), tok.size, rounded=False)
+    y_allow = rounding_allowance(o_ex, token_row, w, s_ex, tok.size)
+    return OracleResult(tok, L, ids, w, xq, xs, bf16_round(y_sum), y_sum, y_allow)
 
 
 def moe_forward_loops(cfg, x_bits, weights: Callable, w_r=None, logits=None) -> np.ndarray:

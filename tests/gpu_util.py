@@ -86,15 +86,19 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
     return np.where(a > 0, np.ldexp(1.0, np.maximum(e - 8, -133)), 0.0)
 
 
-def compare_y(y_gpu: np.ndarray, y_ref: np.ndarray, y_sum: np.ndarray, what: str = "y") -> tuple[float, float]:
+def compare_y(y_gpu: np.ndarray, y_ref: np.ndarray, y_sum: np.ndarray, what: str = "y",
+              allow: np.ndarray | None = None) -> tuple[float, float]:
     """Layer-output tolerance: relative L2 <= 5e-3 against the oracle's BF16 y, and for EVERY element
-    |y_gpu - y_sum| <= 2e-2 * RMS(y_ref) + ulp_bf16 / 2, where y_sum is the oracle's float64 combine sum
+    |y_gpu - y_sum| <= 2e-2 * RMS(y_ref) + ulp_bf16 / 2 + allow, where y_sum is the oracle's float64 combine sum
     before its one BF16 rounding.
 
     The half ulp is the GPU's own final rounding: the GPU output is the BF16 rounding of a value near y_sum,
     and that rounding moves it by at most half a BF16 ulp (taken at the larger of |y_gpu| and |y_sum|, which
-    covers a rounding up into the next binade). Everything else, i.e. the distance of the GPU's unrounded
-    value from the oracle's, must stay within 2e-2 RMS. The literal max |y_gpu - y_ref| / RMS is reported.
+    covers a rounding up into the next binade). ``allow`` is the oracle's rounding_allowance: for the expert
+    outputs whose exact value sits on a BF16 rounding midpoint within float32 precision, either neighbour is a
+    correct rounding, and the other choice moves y by the weight times the BF16 spacing; it is zero for every
+    element whose expert outputs are decided. Everything else, i.e. the distance of the GPU's unrounded value
+    from the oracle's, must stay within 2e-2 RMS. The literal max |y_gpu - y_ref| / RMS is reported.
     """
     y_gpu = np.asarray(y_gpu, np.float64)
     y_ref = np.asarray(y_ref, np.float64)
@@ -108,9 +112,16 @@ def compare_y(y_gpu: np.ndarray, y_ref: np.ndarray, y_sum: np.ndarray, what: str
     mx = float(np.abs(y_gpu - y_ref).max() / max(rms, 1e-300))
     err = np.abs(y_gpu - y_sum)
     bound = MAX_ABS_OVER_RMS * rms + 0.5 * bf16_ulp(np.maximum(np.abs(y_gpu), np.abs(y_sum)))
+    n_allow = 0
+    if allow is not None:
+        allow = np.asarray(allow, np.float64)
+        assert allow.shape == y_sum.shape, f"{what}: allowance shape differs"
+        bound = bound + allow
+        n_allow = int(np.count_nonzero(allow))
     worst = float(np.max(err / np.maximum(bound, 1e-300)))
     say(f"  {what}: rel_l2={rel:.3e} max|y-y_ref|/rms={mx:.3e} "
-        f"max |y-y_sum|/(2e-2 RMS + ulp/2) = {worst:.3f} (n={y_ref.size})")
+        f"max |y-y_sum|/(2e-2 RMS + ulp/2 + straddle allowance) = {worst:.3f} (n={y_ref.size}, "
+        f"{n_allow} elements with an allowance)")
     assert rel <= REL_L2, f"{what}: relative L2 error {rel:.3e} > {REL_L2}"
     assert worst <= 1.0, f"{what}: an element is further than 2e-2 RMS + ulp/2 from the oracle ({worst:.3f} x)"
     return rel, mx

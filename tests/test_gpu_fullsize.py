@@ -133,7 +133,7 @@ def test_full_size_workload(ci):
         xs = layer.ws_view(d, ws, "x_scales").cpu().numpy()[tok]
         np.testing.assert_array_equal(xq, ref.x_codes)
         np.testing.assert_array_equal(xs, ref.x_scales)
-    compare_y(y[tok][keep], ref.y[keep], ref.y_sum[keep], f"y sampled ({keep.size} tokens)")
+    compare_y(y[tok][keep], ref.y[keep], ref.y_sum[keep], f"y sampled ({keep.size} tokens)", ref.y_allow[keep])
     if ci in (2, 3, 4):
         _check_whole_experts(cfg, layer, d, ws, x_bits, offsets)
     del layer, out, ws

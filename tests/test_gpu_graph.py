@@ -85,7 +85,8 @@ def test_graph_replay_matches_eager_and_oracle(name):
     diff = near_tie_tokens(ids, res.ids, res.logits, 2 * LOGIT_TOL)
     keep = np.setdiff1d(np.arange(tok.size), diff)
     assert diff.size <= max(1, tok.size // 100)
-    compare_y(bf16_values(y)[tok][keep], res.y[keep], res.y_sum[keep], f"replayed y vs oracle ({keep.size} tokens)")
+    compare_y(bf16_values(y)[tok][keep], res.y[keep], res.y_sum[keep], f"replayed y vs oracle ({keep.size} tokens)",
+              res.y_allow[keep])
 
     # new input values in the same buffers: the replay follows them
     rng = np.random.default_rng(11)

@@ -97,6 +97,9 @@ CASES = {
                                          K=2, dtype="fp8", T_s=300, logits="uniform"),
     "wide_gateup_ep_fp8": synth.LayerConfig("wide_gateup_ep", T=2048, H=256, F=1920, F_s=1920, E=64, E_loc=8,
                                             e0=0, K=8, dtype="fp8", T_s=200, logits="zipf"),
+    # the same path with F = 24 x 128 + 56: a partial last h slice quantised in the epilogue
+    "wide_gateup_nondiv_fp8": synth.LayerConfig("wide_gateup_nondiv", T=4096, H=256, F=3128, F_s=3128, E=8,
+                                                E_loc=8, e0=0, K=2, dtype="fp8", T_s=300, logits="uniform"),
     "rows_257_fp8": synth.LayerConfig("rows_257_fp8", T=257, H=512, F=256, F_s=0, E=1, E_loc=1, e0=0, K=1,
                                       dtype="fp8", T_s=0, logits="single"),
     "rows_513_bf16": synth.LayerConfig("rows_513_bf16", T=513, H=384, F=128, F_s=128, E=1, E_loc=1, e0=0, K=1,
@@ -135,7 +138,7 @@ def _check_given_logits_path(cfg, layer, x, ref, logits_np):
     # rows with no local pair and no shared expert are exactly zero on both sides
     idle = ~np.any(tr_r >= 0, axis=1) & (np.arange(cfg.T) >= cfg.T_s)
     assert np.all(y[idle] == 0) and np.all(ref.y[idle] == 0)
-    compare_y(y[~idle], ref.y[~idle], ref.y_sum[~idle], "y (given logits)")
+    compare_y(y[~idle], ref.y[~idle], ref.y_sum[~idle], "y (given logits)", ref.y_allow[~idle])
     return out
 
 
@@ -158,7 +161,7 @@ def test_forward_matches_oracle(name):
     diff = near_tie_tokens(ids, ref.ids, ref.logits, 2 * LOGIT_TOL)
     keep = np.setdiff1d(np.arange(cfg.T), diff)
     assert diff.size <= max(1, cfg.T // 100), f"{diff.size} tokens routed differently"
-    compare_y(bf16_values(out["y"])[keep], ref.y[keep], ref.y_sum[keep], "y (own logits)")
+    compare_y(bf16_values(out["y"])[keep], ref.y[keep], ref.y_sum[keep], "y (own logits)", ref.y_allow[keep])
 
 
 def test_forward_is_deterministic():
