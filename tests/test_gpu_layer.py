@@ -201,11 +201,12 @@ def test_zero_tokens_is_a_no_op():
     assert out["y"].shape == (0, cfg.H)
 
 
-@pytest.mark.parametrize("name", ["nondiv_small_fp8", "prefill_small_fp8"])
+@pytest.mark.parametrize("name", ["nondiv_small_fp8", "prefill_small_fp8", "wide_gateup_fp8"])
 def test_separate_entry_points_match_forward(name):
     """route -> permute -> quant -> gateup -> quant -> down -> shared -> combine, one call at a time, bit for bit
     against dmoe_forward on the same logits (weight-streaming and tile GEMMs; the forward runs the shared expert
-    as an extra group of the routed launches, the entry point as a GEMM of its own)."""
+    as an extra group of the routed launches, the entry point as a GEMM of its own; on the wide case the forward
+    quantises h in the gate/up epilogue, the separate calls through dmoe_quant_act)."""
     import fp8_expert_ffn_amd as dm
     cfg, layer, x, x_bits, wr, given, ref = _run(name)
     logits = torch.from_numpy(given if given is not None else ref.logits).to(DEV)
