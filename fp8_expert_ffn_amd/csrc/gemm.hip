@@ -513,10 +513,10 @@ hipError_t launch_fill_offsets(int32_t* offsets, int rows, hipStream_t stream) {
 // quantised in its epilogue, when the host bound on rows per expert reaches
 // DMOE_WIDE_GU (0: never): with many rows per expert its 256-row tiles halve
 // the bytes staged per FLOP and the saved quantise launch pays (EP share, 4096
-// rows per expert: layer 5.59 -> 5.24 ms; dense FFN 1.55 -> 1.48 ms; the vision
-// layer's 512 rows per expert gain nothing, prefill's 256 lose).
+// rows per expert: layer 5.25 -> 5.02 ms; dense FFN 1.48 -> 1.43 ms; vision,
+// 512 rows per expert: 0.813 -> 0.801 ms; prefill's 256 break even).
 #ifndef DMOE_WIDE_GU
-#define DMOE_WIDE_GU 1024
+#define DMOE_WIDE_GU 512
 #endif
 // The GEMM workspace holds two tile schedules, one per tile height:
 // [tiles of 128 rows][count] [tiles of 256 rows][count].

@@ -231,6 +231,12 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
         }
       }
       if constexpr (MODE == kModeFP8X) {
+        // Waves 4-7 (one of the two waves of each SIMD) issue at a raised priority
+        // over the exact-product block: the stage barrier otherwise keeps a SIMD's
+        // two waves in step, converting at the same time and multiplying at the
+        // same time; with one ahead, one converts while the other multiplies
+        // (measured: EP share gate/up 3.62 -> 3.36 ms, dense FFN 1.07 -> 1.02 ms).
+        if (wave_u >= 4) __builtin_amdgcn_s_setprio(3);
         i32x4 a16[MT][4];
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
@@ -258,6 +264,7 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(const TileArgs 
             for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[r], saw[wsel][i], acc[i][j][r]);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
       } else if constexpr (MODE == kModeFP8) {
         // Software pipeline over the column tiles: the MT products of tile j
         // are issued before the promotion of tile j - 1's products, so the

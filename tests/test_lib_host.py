@@ -121,7 +121,7 @@ def test_forward_desc_validation_and_sizes(L):
 
 def test_forward_names_its_gate_up_kernel(L):
     # the launcher's rule, host side only: weight streaming up to 32 rows per expert by the host bound
-    # ceil(T*K / E_loc); FP8 gate/up on the two-workgroup tile kernel below 1024 rows per expert and on the
+    # ceil(T*K / E_loc); FP8 gate/up on the two-workgroup tile kernel below 512 rows per expert and on the
     # wide kernel (h quantised in its epilogue) from there with enough work items; BF16 on the wide kernel
     # from 128 rows per expert with enough work items
     def name(T, H, F, Fs, E, E_loc, K, Ts, dtype):
@@ -131,7 +131,8 @@ def test_forward_names_its_gate_up_kernel(L):
     assert name(8192, 5120, 1536, 1536, 256, 256, 8, 8192, FP8) == "gemm_tile_kernel"
     assert name(16384, 5120, 1536, 1536, 256, 32, 8, 2048, FP8) == "gemm_wide_kernel"
     assert name(4096, 1536, 2112, 0, 64, 64, 8, 0, BF16) == "gemm_wide_kernel"
-    assert name(4096, 1536, 2112, 0, 64, 64, 8, 0, FP8) == "gemm_tile_kernel"
+    assert name(4096, 1536, 2112, 0, 64, 64, 8, 0, FP8) == "gemm_wide_kernel"
+    assert name(4096, 1536, 2112, 0, 128, 128, 8, 0, FP8) == "gemm_tile_kernel"  # 256 rows per expert
     assert name(2048, 5120, 1400, 1400, 256, 256, 8, 2048, FP8) == "gemm_tile_kernel"
     bad = L.LayerDesc(64, 5120, 1536, 1536, 256, 32, 240, 8, 64, 1, 0)  # local experts past E
     assert L.dmoe_forward_gateup_kernel(bad) is None
