@@ -47,6 +47,12 @@ Readings where the pages are silent (each also listed in the design notes):
   roundings of it; ``rounding_allowance`` gives, per output element, what the
   other choice moves y by (weight x spacing), so that a comparison can accept
   either.
+* On the FP8 path each 128-wide block of the down projection is summed on FP8
+  matrix cores and then promoted with its two scales (PR #47844, implementation
+  list: fine-grained FP8 blocks), so an expert output is known only to the
+  accumulation precision of those cores: ``FP8_MMA_REL`` of the sum of the
+  absolute products. There the band around a midpoint is the larger of that
+  and the float32 one.
 
 Functions marked "parity pinned" are checked in the CPU test suite against
 the format definition, library routines, closed forms or brute force.
@@ -63,7 +69,7 @@ __all__ = [
     "E4M3_MAX", "e4m3_values", "e4m3_encode", "bf16_to_f64", "bf16_round",
     "quantize_act", "quantize_weight_blocks", "dequantize_act", "dequantize_weight_blocks",
     "router_logits", "route", "sigmoid_scores", "route_sigmoid", "permute", "swiglu_expert", "combine",
-    "bf16_spacing", "bf16_midpoint_straddle", "rounding_allowance",
+    "bf16_spacing", "bf16_midpoint_straddle", "rounding_allowance", "FP8_MMA_REL",
     "OracleResult", "moe_forward", "moe_forward_loops",
 ]
 
@@ -338,15 +344,17 @@ def _silu(g: np.ndarray) -> np.ndarray:
 
 
 def swiglu_expert(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, fp8: bool,
-                  rounded: bool = True) -> np.ndarray:
+                  rounded: bool = True, abs_terms: bool = False):
     """One expert on rows a: o = bf16(down(q(bf16(silu(a Wg^T) * (a Wu^T))))).
 
     a, wg [F, H], wu [F, H], wd [H, F] are float64 (already dequantised on the
     FP8 path). On the FP8 path the BF16 h is quantised per 1x128 slice and
     dequantised before the down projection. Returns float64 values that are
     exactly bfloat16, or with ``rounded=False`` the float64 down projection
-    before its BF16 rounding. parity pinned (textbook SwiGLU via torch; FP8 h
-    step against torch's float8 cast and hand-made values).
+    before its BF16 rounding; with ``abs_terms`` also the sum of the absolute
+    products of that projection, |h| |Wd|^T. parity pinned (textbook SwiGLU via
+    torch; FP8 h step against torch's float8 cast and hand-made values;
+    absolute sums by loops).
     """
     g = a @ wg.T
     u = a @ wu.T
@@ -355,7 +363,16 @@ def swiglu_expert(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
         qh, sh = quantize_act(h)
         h = dequantize_act(qh, sh)
     o = h @ wd.T
-    return bf16_round(o) if rounded else o
+    o = bf16_round(o) if rounded else o
+    return (o, np.abs(h) @ np.abs(wd).T) if abs_terms else o
+
+
+# Accumulation precision of one 128-wide block sum on FP8 matrix cores, as a fraction of the sum of the
+# absolute products: 2^-13 (1.2e-4) bounds the largest error measured for one 128-term E4M3 instruction on
+# gfx950 matrix cores against the exact sum (1.1e-4, with operands spread over the whole exponent range;
+# 1.9e-5 in the normal range). A block's scales multiply its error and its absolute sum alike, so the bound
+# holds for the promoted sum over all blocks.
+FP8_MMA_REL = 2.0 ** -13
 
 
 def bf16_spacing(v: np.ndarray) -> np.ndarray:
@@ -364,32 +381,37 @@ def bf16_spacing(v: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.floor(np.log2(np.where(a > 0, a, 1.0))) - 7)
 
 
-def bf16_midpoint_straddle(v: np.ndarray, rel: float = 2.0 ** -18) -> np.ndarray:
-    """True where the exact value v lies within rel * |v| of a midpoint between two adjacent bfloat16 values.
+def bf16_midpoint_straddle(v: np.ndarray, rel: float = 2.0 ** -18, band: np.ndarray | None = None) -> np.ndarray:
+    """True where the exact value v lies within max(rel * |v|, band) of a midpoint between two adjacent
+    bfloat16 values.
 
     A sum of thousands of products carried out in float32 (or on matrix cores with float32 accumulation) is
     only known to about that relative precision, so such a value can legitimately be rounded to either of
-    its two bfloat16 neighbours.
+    its two bfloat16 neighbours; ``band`` (same shape as v, or None) widens that to an absolute precision,
+    e.g. that of a sum formed on FP8 matrix cores.
     """
     v = np.asarray(v, dtype=np.float64)
     a = np.abs(v)
     u = bf16_spacing(v)
     q = a / u
     dist = np.abs(q - np.floor(q) - 0.5) * u
-    return (a > 0) & (dist <= rel * a)
+    tol = rel * a if band is None else np.maximum(rel * a, np.asarray(band, dtype=np.float64))
+    return (a > 0) & (dist <= tol)
 
 
 def rounding_allowance(o_exact: np.ndarray, token_row: np.ndarray, w: np.ndarray, s_exact: np.ndarray | None,
-                       t_s: int) -> np.ndarray:
+                       t_s: int, o_band: np.ndarray | None = None, s_band: np.ndarray | None = None) -> np.ndarray:
     """Per output element: sum over the routed pairs (and the shared expert) of |weight| x the bfloat16
     spacing of those expert outputs whose exact value straddles a rounding midpoint (bf16_midpoint_straddle).
 
     The layer rounds every expert output to bfloat16 before the weighted sum; where the exact value sits on a
     midpoint within float32 precision, either neighbour is a correct rounding, and the two choices move y by
-    the weight times the spacing. Elements far from a midpoint get no allowance.
+    the weight times the spacing. Elements far from a midpoint get no allowance. ``o_band``/``s_band`` are the
+    absolute precision bands of the expert outputs (bf16_midpoint_straddle's ``band``), or None.
     """
-    oa = np.where(bf16_midpoint_straddle(o_exact), bf16_spacing(o_exact), 0.0)
-    sa = None if s_exact is None else np.where(bf16_midpoint_straddle(s_exact), bf16_spacing(s_exact), 0.0)
+    oa = np.where(bf16_midpoint_straddle(o_exact, band=o_band), bf16_spacing(o_exact), 0.0)
+    sa = None if s_exact is None else np.where(bf16_midpoint_straddle(s_exact, band=s_band),
+                                               bf16_spacing(s_exact), 0.0)
     return combine(oa, token_row, np.abs(np.asarray(w, dtype=np.float64)), sa, t_s, rounded=False)
 
 
@@ -476,20 +498,33 @@ def moe_forward(cfg, x_bits: np.ndarray, weights: Callable, w_r: np.ndarray | No
         xq = xs = None
         a_all = x
     o_ex = np.zeros((int(offsets[-1]), cfg.H), dtype=np.float64)  # expert outputs before their BF16 rounding
+    # FP8: absolute precision band of each expert output (FP8_MMA_REL x its sum of absolute products)
+    o_band = np.zeros_like(o_ex) if fp8 else None
     for el in range(cfg.E_loc):
         r0, r1 = int(offsets[el]), int(offsets[el + 1])
         if r1 == r0:
             continue
         wg, wu, wd = _expert_weights(cfg, weights, cfg.e0 + el, fp8)
-        o_ex[r0:r1] = swiglu_expert(a_all[row_token[r0:r1]], wg, wu, wd, fp8, rounded=False)
+        if fp8:
+            o_ex[r0:r1], ab = swiglu_expert(a_all[row_token[r0:r1]], wg, wu, wd, fp8, rounded=False,
+                                            abs_terms=True)
+            o_band[r0:r1] = FP8_MMA_REL * ab
+        else:
+            o_ex[r0:r1] = swiglu_expert(a_all[row_token[r0:r1]], wg, wu, wd, fp8, rounded=False)
     shared_rows = tok < cfg.T_s
     s_ex = np.zeros((tok.size, cfg.H), dtype=np.float64)
+    s_band = np.zeros_like(s_ex) if fp8 else None
     if shared_rows.any():
         wg, wu, wd = _expert_weights(cfg, weights, -1, fp8)
-        s_ex[shared_rows] = swiglu_expert(a_all[shared_rows], wg, wu, wd, fp8, rounded=False)
+        if fp8:
+            s_ex[shared_rows], ab = swiglu_expert(a_all[shared_rows], wg, wu, wd, fp8, rounded=False,
+                                                  abs_terms=True)
+            s_band[shared_rows] = FP8_MMA_REL * ab
+        else:
+            s_ex[shared_rows] = swiglu_expert(a_all[shared_rows], wg, wu, wd, fp8, rounded=False)
     # rows of s past T_s are zero
     y_sum = combine(bf16_round(o_ex), token_row, w, bf16_round(s_ex), tok.size, rounded=False)
-    y_allow = rounding_allowance(o_ex, token_row, w, s_ex, tok.size)
+    y_allow = rounding_allowance(o_ex, token_row, w, s_ex, tok.size, o_band, s_band)
     return OracleResult(tok, L, ids, w, xq, xs, bf16_round(y_sum), y_sum, y_allow)
 
 

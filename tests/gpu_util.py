@@ -95,9 +95,10 @@ def compare_y(y_gpu: np.ndarray, y_ref: np.ndarray, y_sum: np.ndarray, what: str
     The half ulp is the GPU's own final rounding: the GPU output is the BF16 rounding of a value near y_sum,
     and that rounding moves it by at most half a BF16 ulp (taken at the larger of |y_gpu| and |y_sum|, which
     covers a rounding up into the next binade). ``allow`` is the oracle's rounding_allowance: for the expert
-    outputs whose exact value sits on a BF16 rounding midpoint within float32 precision, either neighbour is a
-    correct rounding, and the other choice moves y by the weight times the BF16 spacing; it is zero for every
-    element whose expert outputs are decided. Everything else, i.e. the distance of the GPU's unrounded value
+    outputs whose exact value sits on a BF16 rounding midpoint within the precision of their sum (float32, or
+    on the FP8 path the FP8 matrix cores' block sums), either neighbour is a correct rounding, and the other
+    choice moves y by the weight times the BF16 spacing; it is zero for every element whose expert outputs are
+    decided. Everything else, i.e. the distance of the GPU's unrounded value
     from the oracle's, must stay within 2e-2 RMS. The literal max |y_gpu - y_ref| / RMS is reported.
     """
     y_gpu = np.asarray(y_gpu, np.float64)
@@ -138,3 +139,49 @@ def near_tie_tokens(ids_gpu: np.ndarray, ids_ref: np.ndarray, logits_ref: np.nda
             assert abs(float(logits_ref[t, e]) - float(kth)) <= tol, \
                 f"token {t}: expert {e} differs but is not a near tie ({logits_ref[t, e]} vs {kth})"
     return diff
+
+
+def check_given_logits_path(cfg, layer, x, ref, logits_np):
+    """Same logits on both sides: routing, permutation and x codes must be bit-exact."""
+    out = layer.forward(x, cfg.T_s, logits=torch.from_numpy(logits_np).to(DEV))
+    torch.cuda.synchronize()
+    d, p, ws = out["_call"]
+    np.testing.assert_array_equal(out["topk_ids"].cpu().numpy(), ref.ids)
+    assert np.max(np.abs(out["topk_w"].cpu().numpy().astype(np.float64) - ref.w)) <= W_TOL
+    off_r, rt_r, rs_r, tr_r = oracle.permute(ref.ids, cfg.e0, cfg.E_loc)
+    M = int(off_r[-1])
+    np.testing.assert_array_equal(layer.ws_view(d, ws, "offsets").cpu().numpy(), off_r)
+    np.testing.assert_array_equal(layer.ws_view(d, ws, "row_token").cpu().numpy()[:M], rt_r)
+    np.testing.assert_array_equal(layer.ws_view(d, ws, "row_slot").cpu().numpy()[:M], rs_r)
+    np.testing.assert_array_equal(layer.ws_view(d, ws, "token_row").cpu().numpy(), tr_r)
+    if cfg.dtype == "fp8":
+        np.testing.assert_array_equal(layer.ws_view(d, ws, "x_codes").cpu().numpy(), ref.x_codes)
+        np.testing.assert_array_equal(layer.ws_view(d, ws, "x_scales").cpu().numpy(), ref.x_scales)
+    y = bf16_values(out["y"])
+    # rows with no local pair and no shared expert are exactly zero on both sides
+    idle = ~np.any(tr_r >= 0, axis=1) & (np.arange(cfg.T) >= cfg.T_s)
+    assert np.all(y[idle] == 0) and np.all(ref.y[idle] == 0)
+    compare_y(y[~idle], ref.y[~idle], ref.y_sum[~idle], "y (given logits)", ref.y_allow[~idle])
+    return out
+
+
+def check_forward(cfg, layer, x, wr, given, ref):
+    """Both legs of the layer check: the oracle's (or the given) logits handed to the GPU, then, for router
+    workloads, the full path with the GPU's own router logits (near ties may route differently)."""
+    if given is not None:
+        check_given_logits_path(cfg, layer, x, ref, given)
+        return
+    # 1) the oracle's logits given to the GPU: exact routing, tolerance on y
+    check_given_logits_path(cfg, layer, x, ref, ref.logits)
+    # 2) the full path with the GPU's own router logits
+    out = layer.forward(x, cfg.T_s, w_router=torch.from_numpy(wr).to(DEV))
+    torch.cuda.synchronize()
+    L = out["logits"].cpu().numpy()
+    err = float(np.max(np.abs(L.astype(np.float64) - ref.logits)))
+    say(f"  router logits max |dL| = {err:.3e}")
+    assert err <= LOGIT_TOL
+    ids = out["topk_ids"].cpu().numpy()
+    diff = near_tie_tokens(ids, ref.ids, ref.logits, 2 * LOGIT_TOL)
+    keep = np.setdiff1d(np.arange(cfg.T), diff)
+    assert diff.size <= max(1, cfg.T // 100), f"{diff.size} tokens routed differently"
+    compare_y(bf16_values(out["y"])[keep], ref.y[keep], ref.y_sum[keep], "y (own logits)", ref.y_allow[keep])
