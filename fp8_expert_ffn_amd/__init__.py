@@ -10,7 +10,7 @@ from ._lib import (  # noqa: F401
     dmoe_router_logits, dmoe_route, dmoe_route_grouped, dmoe_route_sigmoid, dmoe_permute, dmoe_quant_act, dmoe_quant_weight_blocks,
     dmoe_gemm_ws_bytes, dmoe_grouped_gemm_gateup, dmoe_grouped_gemm_down, dmoe_shared_expert,
     dmoe_combine, dmoe_forward, dmoe_forward_timed, dmoe_forward_ws_bytes, dmoe_forward_ws_offset,
-    dmoe_forward_gateup_kernel,
+    dmoe_forward_gateup_kernel, dmoe_forward_down_kernel,
     DMOE_STAGES, STAGE_NAMES,
 )
 from .layer import MoELayer  # noqa: F401

@@ -33,7 +33,7 @@ EXPORTS = [
     "dmoe_permute", "dmoe_quant_act", "dmoe_quant_weight_blocks", "dmoe_gemm_ws_bytes",
     "dmoe_grouped_gemm_gateup", "dmoe_grouped_gemm_down", "dmoe_shared_expert_ws_bytes", "dmoe_shared_expert",
     "dmoe_combine", "dmoe_forward_ws_bytes", "dmoe_forward", "dmoe_forward_timed", "dmoe_forward_ws_offset",
-    "dmoe_forward_gateup_kernel", "dmoe_forward_noalloc",
+    "dmoe_forward_gateup_kernel", "dmoe_forward_down_kernel", "dmoe_forward_noalloc",
 ]
 DMOE_STAGES = 9
 STAGE_NAMES = ["router_logits", "route", "permute", "quant_x", "gateup", "quant_h", "down", "shared", "combine"]
@@ -93,6 +93,7 @@ _SIGS = {
     "dmoe_forward_timed": ([ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerPtrs), P, SZ, P, P], I32),
     "dmoe_forward_ws_offset": ([ctypes.POINTER(LayerDesc), I32], I64),
     "dmoe_forward_gateup_kernel": ([ctypes.POINTER(LayerDesc)], ctypes.c_char_p),
+    "dmoe_forward_down_kernel": ([ctypes.POINTER(LayerDesc)], ctypes.c_char_p),
     "dmoe_forward_noalloc": ([ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerPtrs), P], I32),
 }
 
@@ -283,6 +284,11 @@ def dmoe_forward_ws_offset(desc: LayerDesc, which: int) -> int:
 
 def dmoe_forward_gateup_kernel(desc: LayerDesc) -> str | None:
     name = lib().dmoe_forward_gateup_kernel(ctypes.byref(desc))
+    return name.decode() if name is not None else None
+
+
+def dmoe_forward_down_kernel(desc: LayerDesc) -> str | None:
+    name = lib().dmoe_forward_down_kernel(ctypes.byref(desc))
     return name.decode() if name is not None else None
 
 

@@ -506,6 +506,12 @@ const char* dmoe_forward_gateup_kernel(const dmoe_layer_desc* desc) {
   return gemm_gateup_kernel_name(desc->dtype, mcap, desc->E_loc, fuse_shared(desc) ? desc->T_s : 0, desc->F);
 }
 
+const char* dmoe_forward_down_kernel(const dmoe_layer_desc* desc) {
+  if (check_desc(desc) != DMOE_OK) return nullptr;
+  const int mcap = desc->T * desc->K;
+  return gemm_down_kernel_name(desc->dtype, mcap, desc->E_loc, fuse_shared(desc) ? desc->T_s : 0, desc->H);
+}
+
 int64_t dmoe_forward_ws_offset(const dmoe_layer_desc* desc, int32_t which) {
   if (check_desc(desc) != DMOE_OK || which < 0 || which > W_S) return -1;
   return fwd_layout(desc).off[which];

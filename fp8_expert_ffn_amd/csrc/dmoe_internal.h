@@ -112,6 +112,7 @@ bool gemm_uses_stream(int max_rows, int E_loc);
 bool gemm_fuses_h_quant(int max_rows, int E_loc, int extra_rows, int N);
 // name of the kernel a gate/up launch of this shape runs (the launcher's rule)
 const char* gemm_gateup_kernel_name(int dtype, int max_rows, int E_loc, int extra_rows, int N);
+const char* gemm_down_kernel_name(int dtype, int max_rows, int E_loc, int extra_rows, int N);
 hipError_t launch_gemm_gateup(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_fill_offsets(int32_t* offsets, int rows, hipStream_t stream);

@@ -576,6 +576,12 @@ const char* gemm_gateup_kernel_name(int dtype, int max_rows, int E_loc, int extr
                                                                                : "gemm_tile_kernel";
 }
 
+const char* gemm_down_kernel_name(int dtype, int max_rows, int E_loc, int extra_rows, int N) {
+  if (gemm_uses_stream(max_rows, E_loc)) return "gemm_stage_kernel";
+  return use_wide(dtype, false, max_rows, E_loc, extra_rows, round_up(N, 128)) ? "gemm_wide_kernel"
+                                                                                : "gemm_tile_kernel";
+}
+
 bool gemm_fuses_h_quant(int max_rows, int E_loc, int extra_rows, int N) {
   return DMOE_WIDE_GU > 0 && !gemm_uses_stream(max_rows, E_loc) &&
          use_wide(DMOE_FP8_E4M3, true, max_rows, E_loc, extra_rows, round_up(N, 128));

@@ -398,6 +398,14 @@ int64_t dmoe_forward_ws_offset(const dmoe_layer_desc* desc, int32_t which);
 const char* dmoe_forward_gateup_kernel(const dmoe_layer_desc* desc);
 
 /*
+ * Name of the GEMM kernel that the layer's down launch (routed experts, and
+ * the shared expert when it runs as an extra group of the routed launches, as
+ * it does when F_s == F) runs for this desc, from the same three (a static
+ * string; NULL for an invalid desc). For profiling and reports; no GPU work.
+ */
+const char* dmoe_forward_down_kernel(const dmoe_layer_desc* desc);
+
+/*
  * dmoe_forward without a caller workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc). The workspace is a fixed device array inside the

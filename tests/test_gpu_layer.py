@@ -8,8 +8,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import (DEV, LOGIT_TOL, W_TOL, bf16_values, build_layer, compare_y, layer_inputs, near_tie_tokens, say,
-                      score_bias_of, to_dev_bf16, weights_provider)
+from gpu_util import (DEV, W_TOL, bf16_values, build_layer, check_forward, check_given_logits_path, compare_y,
+                      layer_inputs, say, score_bias_of, to_dev_bf16, weights_provider)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,12 +84,24 @@ CASES = {
                                        dtype="fp8", T_s=40, logits="uniform"),
     "small_ep_bf16": synth.LayerConfig("small_ep", T=16, H=1024, F=256, F_s=256, E=256, E_loc=32, e0=32, K=8,
                                        dtype="bf16", T_s=16, logits="zipf"),
-    # several 256-row tiles per expert on the wide tile GEMM (about 500 rows per expert: a full tile and a
-    # ragged one), and one expert of 257 or 513 rows (a last tile of one row)
-    "wide_tiles_fp8": synth.LayerConfig("wide_tiles_fp8", T=2000, H=512, F=384, F_s=384, E=8, E_loc=8, e0=0, K=2,
+    # several 128-row tiles per expert on the two-workgroup tile GEMM (about 500 rows per expert, too few work
+    # items for the wide kernel: full tiles and a ragged one), and one expert of 257 or 513 rows (a last tile
+    # of one row)
+    "many_tiles_fp8": synth.LayerConfig("many_tiles_fp8", T=2000, H=512, F=384, F_s=384, E=8, E_loc=8, e0=0, K=2,
                                         dtype="fp8", T_s=700, logits="router"),
-    "wide_tiles_bf16": synth.LayerConfig("wide_tiles_bf16", T=1500, H=768, F=256, F_s=256, E=6, E_loc=6, e0=0,
+    "many_tiles_bf16": synth.LayerConfig("many_tiles_bf16", T=1500, H=768, F=256, F_s=256, E=6, E_loc=6, e0=0,
                                          K=2, dtype="bf16", T_s=1500, logits="uniform"),
+    # the down projection on the wide tile GEMM (at least 128 rows per expert by the host bound and at least
+    # 1024 work items: (20 + 40 + 3) 256-row tiles x 20 column blocks): experts of about 128 rows in one partly
+    # filled tile each, and the shared rows as an extra group in tiles of 256, 256 and 128 (FP8) or 244 (BF16)
+    "wide_down_fp8": synth.LayerConfig("wide_down_fp8", T=640, H=5120, F=256, F_s=256, E=40, E_loc=40, e0=0, K=8,
+                                       dtype="fp8", T_s=640, logits="uniform"),
+    "wide_down_bf16": synth.LayerConfig("wide_down_bf16", T=640, H=5120, F=384, F_s=384, E=40, E_loc=40, e0=0,
+                                        K=8, dtype="bf16", T_s=500, logits="router"),
+    # BF16 gate/up on the wide tile GEMM (1024 rows per expert by the host bound, 42 tiles x 25 column blocks),
+    # with Zipf-skewed experts of a few to thousands of rows
+    "wide_gateup_bf16": synth.LayerConfig("wide_gateup_bf16", T=4096, H=256, F=3200, F_s=3200, E=8, E_loc=8, e0=0,
+                                          K=2, dtype="bf16", T_s=300, logits="zipf"),
     # FP8 gate/up on the wide tile GEMM with h quantised in its epilogue (at least 1024 rows per expert by the
     # host bound and 1024 work items): uniform routing with a ragged shared-expert tail, and a Zipf-skewed EP
     # share whose experts range from a few to thousands of rows
@@ -118,50 +130,10 @@ def _run(name):
     return cfg, layer, x, x_bits, wr, given, ref
 
 
-def _check_given_logits_path(cfg, layer, x, ref, logits_np):
-    """Same logits on both sides: routing, permutation and x codes must be bit-exact."""
-    out = layer.forward(x, cfg.T_s, logits=torch.from_numpy(logits_np).to(DEV))
-    torch.cuda.synchronize()
-    d, p, ws = out["_call"]
-    np.testing.assert_array_equal(out["topk_ids"].cpu().numpy(), ref.ids)
-    assert np.max(np.abs(out["topk_w"].cpu().numpy().astype(np.float64) - ref.w)) <= W_TOL
-    off_r, rt_r, rs_r, tr_r = oracle.permute(ref.ids, cfg.e0, cfg.E_loc)
-    M = int(off_r[-1])
-    np.testing.assert_array_equal(layer.ws_view(d, ws, "offsets").cpu().numpy(), off_r)
-    np.testing.assert_array_equal(layer.ws_view(d, ws, "row_token").cpu().numpy()[:M], rt_r)
-    np.testing.assert_array_equal(layer.ws_view(d, ws, "row_slot").cpu().numpy()[:M], rs_r)
-    np.testing.assert_array_equal(layer.ws_view(d, ws, "token_row").cpu().numpy(), tr_r)
-    if cfg.dtype == "fp8":
-        np.testing.assert_array_equal(layer.ws_view(d, ws, "x_codes").cpu().numpy(), ref.x_codes)
-        np.testing.assert_array_equal(layer.ws_view(d, ws, "x_scales").cpu().numpy(), ref.x_scales)
-    y = bf16_values(out["y"])
-    # rows with no local pair and no shared expert are exactly zero on both sides
-    idle = ~np.any(tr_r >= 0, axis=1) & (np.arange(cfg.T) >= cfg.T_s)
-    assert np.all(y[idle] == 0) and np.all(ref.y[idle] == 0)
-    compare_y(y[~idle], ref.y[~idle], ref.y_sum[~idle], "y (given logits)", ref.y_allow[~idle])
-    return out
-
-
 @pytest.mark.parametrize("name", list(CASES))
 def test_forward_matches_oracle(name):
     cfg, layer, x, x_bits, wr, given, ref = _run(name)
-    if given is not None:
-        _check_given_logits_path(cfg, layer, x, ref, given)
-        return
-    # 1) the oracle's logits given to the GPU: exact routing, tolerance on y
-    _check_given_logits_path(cfg, layer, x, ref, ref.logits)
-    # 2) the full path with the GPU's own router logits
-    out = layer.forward(x, cfg.T_s, w_router=torch.from_numpy(wr).to(DEV))
-    torch.cuda.synchronize()
-    L = out["logits"].cpu().numpy()
-    err = float(np.max(np.abs(L.astype(np.float64) - ref.logits)))
-    say(f"  router logits max |dL| = {err:.3e}")
-    assert err <= LOGIT_TOL
-    ids = out["topk_ids"].cpu().numpy()
-    diff = near_tie_tokens(ids, ref.ids, ref.logits, 2 * LOGIT_TOL)
-    keep = np.setdiff1d(np.arange(cfg.T), diff)
-    assert diff.size <= max(1, cfg.T // 100), f"{diff.size} tokens routed differently"
-    compare_y(bf16_values(out["y"])[keep], ref.y[keep], ref.y_sum[keep], "y (own logits)", ref.y_allow[keep])
+    check_forward(cfg, layer, x, wr, given, ref)
 
 
 def test_forward_is_deterministic():
@@ -189,7 +161,7 @@ def test_all_tokens_on_one_expert_and_empty_experts(dtype, K):
     L[:, 12] = np.linspace(-2, -1.5, cfg.T).astype(np.float32)
     L[:, 20] = -3.0
     ref = oracle.moe_forward(cfg, x_bits, weights_provider(cfg), logits=L)
-    _check_given_logits_path(cfg, layer, to_dev_bf16(x_bits), ref, L)
+    check_given_logits_path(cfg, layer, to_dev_bf16(x_bits), ref, L)
 
 
 def test_zero_tokens_is_a_no_op():

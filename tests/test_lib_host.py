@@ -134,8 +134,36 @@ def test_forward_names_its_gate_up_kernel(L):
     assert name(4096, 1536, 2112, 0, 64, 64, 8, 0, FP8) == "gemm_wide_kernel"
     assert name(4096, 1536, 2112, 0, 128, 128, 8, 0, FP8) == "gemm_tile_kernel"  # 256 rows per expert
     assert name(2048, 5120, 1400, 1400, 256, 256, 8, 2048, FP8) == "gemm_tile_kernel"
+    import test_gpu_layer as gl
+    for case in ("wide_gateup_fp8", "wide_gateup_ep_fp8", "wide_gateup_nondiv_fp8", "wide_gateup_bf16"):
+        c = gl.CASES[case]
+        dt = FP8 if c.dtype == "fp8" else BF16
+        assert name(c.T, c.H, c.F, c.F_s, c.E, c.E_loc, c.K, c.T_s, dt) == "gemm_wide_kernel", case
     bad = L.LayerDesc(64, 5120, 1536, 1536, 256, 32, 240, 8, 64, 1, 0)  # local experts past E
     assert L.dmoe_forward_gateup_kernel(bad) is None
+    assert L.dmoe_forward_down_kernel(bad) is None
+
+
+def test_forward_names_its_down_kernel(L):
+    # down: weight streaming up to 32 rows per expert by the host bound, the wide kernel from 128 rows per
+    # expert with at least 1024 (256-row tile, 256-column block) work items, else the two-workgroup kernel
+    def name(T, H, F, Fs, E, E_loc, K, Ts, dtype):
+        return L.dmoe_forward_down_kernel(L.LayerDesc(T, H, F, Fs, E, E_loc, 0, K, Ts, dtype, 0))
+    FP8, BF16 = L._lib.DMOE_FP8_E4M3, L._lib.DMOE_BF16
+    assert name(64, 5120, 1536, 1536, 256, 256, 8, 64, BF16) == "gemm_stage_kernel"  # decode
+    assert name(128, 5120, 1536, 1536, 256, 256, 8, 128, FP8) == "gemm_stage_kernel"  # verify
+    assert name(8192, 5120, 1536, 1536, 256, 256, 8, 8192, FP8) == "gemm_wide_kernel"  # prefill
+    assert name(16384, 5120, 1536, 1536, 256, 32, 8, 2048, FP8) == "gemm_wide_kernel"  # EP share
+    assert name(2048, 5120, 1400, 1400, 256, 256, 8, 2048, FP8) == "gemm_tile_kernel"  # 64 rows per expert
+    assert name(4096, 5120, 13824, 0, 1, 1, 1, 0, FP8) == "gemm_tile_kernel"  # dense FFN: 340 work items
+    assert name(4096, 1536, 2112, 0, 64, 64, 8, 0, BF16) == "gemm_wide_kernel"  # vision
+    # the reduced parity cases meant for the wide kernel, and the many-tile ones that stay on the tile kernel
+    import test_gpu_layer as gl
+    for case, kernel in (("wide_down_fp8", "gemm_wide_kernel"), ("wide_down_bf16", "gemm_wide_kernel"),
+                         ("many_tiles_fp8", "gemm_tile_kernel"), ("many_tiles_bf16", "gemm_tile_kernel")):
+        c = gl.CASES[case]
+        dt = FP8 if c.dtype == "fp8" else BF16
+        assert name(c.T, c.H, c.F, c.F_s, c.E, c.E_loc, c.K, c.T_s, dt) == kernel, case
 
 
 def test_combine_rejects_bad_slot_count_and_width(L):
