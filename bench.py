@@ -416,6 +416,7 @@ def main() -> int:
                   "TFLOPs": round(acc["flops"] / sec / 1e12, 2),
                   "frac_hbm": round(acc["bytes"] / sec / 1e9 / PEAK_HBM_GBPS, 4),
                   "frac_mfma": round(acc["flops"] / sec / 1e12 / PEAK_TFLOPS[cfg.dtype], 4)},
+        "kernels": {"gateup": kbase, "down": dml.dmoe_forward_down_kernel(d)},
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "stages_note": "separate pass with an event at every stage boundary (markers add a few us each)",
         "roofline": roof,
