@@ -112,6 +112,21 @@ CASES = {
     # the same path with F = 24 x 128 + 56: a partial last h slice quantised in the epilogue
     "wide_gateup_nondiv_fp8": synth.LayerConfig("wide_gateup_nondiv", T=4096, H=256, F=3128, F_s=3128, E=8,
                                                 E_loc=8, e0=0, K=2, dtype="fp8", T_s=300, logits="uniform"),
+    # limits of the descriptor: 1024 experts with top-64 (weight streaming, 4 rows per expert), every expert
+    # selected (K = E), and the FP8 limits H = 16384 or F = 16384 (128 scale slices along K) on the streaming
+    # and the tile kernels
+    "max_experts_fp8": synth.LayerConfig("max_experts_fp8", T=64, H=128, F=64, F_s=64, E=1024, E_loc=1024, e0=0,
+                                         K=64, dtype="fp8", T_s=64, logits="uniform"),
+    "all_experts_bf16": synth.LayerConfig("all_experts_bf16", T=40, H=256, F=136, F_s=136, E=8, E_loc=8, e0=0, K=8,
+                                          dtype="bf16", T_s=40, logits="router"),
+    "max_hidden_stream_fp8": synth.LayerConfig("max_hidden_stream_fp8", T=24, H=16384, F=128, F_s=128, E=4,
+                                               E_loc=4, e0=0, K=2, dtype="fp8", T_s=24, logits="uniform"),
+    "max_hidden_tile_fp8": synth.LayerConfig("max_hidden_tile_fp8", T=200, H=16384, F=128, F_s=128, E=4, E_loc=4,
+                                             e0=0, K=2, dtype="fp8", T_s=200, logits="uniform"),
+    "max_ffn_stream_fp8": synth.LayerConfig("max_ffn_stream_fp8", T=24, H=128, F=16384, F_s=16384, E=4, E_loc=4,
+                                            e0=0, K=2, dtype="fp8", T_s=24, logits="uniform"),
+    "max_ffn_tile_fp8": synth.LayerConfig("max_ffn_tile_fp8", T=200, H=128, F=16384, F_s=16384, E=4, E_loc=4, e0=0,
+                                          K=2, dtype="fp8", T_s=200, logits="uniform"),
     "rows_257_fp8": synth.LayerConfig("rows_257_fp8", T=257, H=512, F=256, F_s=0, E=1, E_loc=1, e0=0, K=1,
                                       dtype="fp8", T_s=0, logits="single"),
     "rows_513_bf16": synth.LayerConfig("rows_513_bf16", T=513, H=384, F=128, F_s=128, E=1, E_loc=1, e0=0, K=1,
